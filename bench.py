@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Headline benchmark: exact causal GQA attention, forward + backward, on one MI355X.
+
+One step = attn_fwd then attn_bwd (every kernel of the path) on one batch of
+seeded synthetic inputs that are already resident in HBM. Default workload:
+the Llama-2-70B attention layer shape, B=1, Hq=64, Hkv=8, S=4096, D=128,
+bf16, scale 1/sqrt(128).
+
+Throughput counts 4*B*Hq*S^2*D FLOPs for the forward pass and 2.5x that for
+the backward pass, halved for the causal mask. Per-kernel durations come from
+HIP events recorded on the launch stream around every kernel of every timed
+step. Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 bf16 flop/clk x 2.4 GHz (AMD's 2.5 PFLOP/s dense figure)
+PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (the runtime torch already loaded)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7", mode=ctypes.RTLD_GLOBAL)
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def check(self, err, what):
+        if err != 0:
+            raise RuntimeError(f"{what} failed with HIP error {err}")
+
+    def event(self):
+        e = ctypes.c_void_p()
+        self.check(self.lib.hipEventCreate(ctypes.byref(e)), "hipEventCreate")
+        return e.value
+
+    def record(self, ev, stream):
+        self.check(self.lib.hipEventRecord(ev, stream), "hipEventRecord")
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        self.check(self.lib.hipEventElapsedTime(ctypes.byref(out), a, b), "hipEventElapsedTime")
+        return float(out.value)
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tiled_attention_memory_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(kernel)
+    if not rec or rec.get("workload") != workload or rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, n_groups):
+    """The fp64 oracle, untuned, on a bounded sample: whole GQA groups of the same workload."""
+    import numpy as np
+    from oracle import attention as att
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    q, k, v, do = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    groups = [(0, g) for g in range(n_groups)]
+    t0 = time.perf_counter()
+    att.backward(q, k, v, do, w.scale, causal=True, heads=groups)
+    dt = time.perf_counter() - t0
+    heads = n_groups * w.group
+    flops = (w.fwd_flops() + w.bwd_flops()) * heads / (w.B * w.Hq)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, forward+backward of {n_groups} of the {w.B * w.Hkv} GQA "
+                      f"groups ({heads} of {w.B * w.Hq} query heads) of the same workload, "
+                      f"{dt:.1f} s wall; counted FLOPs of that sample"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama2_70b_layer_s4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-groups", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the attention path shards by independent (batch, kv-head) "
+              f"groups with no exchange, and this build runs on a single MI355X; --gpus {args.gpus} "
+              f"is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import tiled_attention_memory_amd as tam
+    from tiled_attention_memory_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tam.load()  # fail loudly if the HIP library is missing
+    w = wl.BY_NAME[args.workload]
+    log(f"[bench] workload {w.name}: {w.describe()}")
+    x = wl.workload_inputs(w)
+    dev = {n: torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(torch.bfloat16).cuda()
+           for n in x}
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = tam.workspace_for(q, k)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(ev_f=None, ev_b=None):
+        if ev_f:
+            hip.record(ev_f[0], sh)
+        tam.attn_fwd(q, k, v, o, lse, causal=True, scale=w.scale, stream=stream)
+        if ev_f:
+            hip.record(ev_f[1], sh)
+        tam.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=True, scale=w.scale,
+                     stream=stream, events=ev_b)
+
+    hip = Hip()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev_f = [(hip.event(), hip.event()) for _ in range(K)]
+    ev_b = [(ctypes.c_void_p * tam.BWD_EVENTS)(*[hip.event() for _ in range(tam.BWD_EVENTS)])
+            for _ in range(K)]
+    e0, e1 = hip.event(), hip.event()
+    log(f"[bench] {args.warmup} warmup steps done; timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.record(e0, sh)
+    for i in range(K):
+        step(ev_f[i], ev_b[i])
+    hip.record(e1, sh)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = hip.ms(e0, e1)
+
+    def avg(pairs):
+        return sum(hip.ms(a, b) for a, b in pairs) / len(pairs)
+
+    per = {
+        "attn_fwd_kernel": avg(ev_f),
+        "attn_bwd_prep_kernel": avg([(e[0], e[1]) for e in ev_b]),
+        "attn_bwd_dq_kernel": avg([(e[1], e[2]) for e in ev_b]),
+        "attn_bwd_dkdv_kernel": avg([(e[2], e[3]) for e in ev_b]),
+        "attn_bwd_reduce_kernel": avg([(e[3], e[4]) for e in ev_b]),
+    }
+    for a, b in ev_f:
+        hip.destroy(a)
+        hip.destroy(b)
+    for e in ev_b:
+        for j in range(tam.BWD_EVENTS):
+            hip.destroy(e[j])
+
+    ms_step = total_ms / K
+    flops = w.fwd_flops() + w.bwd_flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    # Algorithmic FLOPs each kernel carries out of the counted total: the forward
+    # kernel's two products; the dK/dV kernel's recomputed S and dP plus dV and dK;
+    # the dQ kernel's dQ. Executed FLOPs add the dQ kernel's second recomputation
+    # of S and dP, its exact-Delta correction product and the lo halves of the
+    # split bf16 operands (dV, dK, dQ).
+    alg_flops = {
+        "attn_fwd_kernel": w.fwd_flops(),
+        "attn_bwd_dkdv_kernel": 2 * w.fwd_flops(),
+        "attn_bwd_dq_kernel": w.fwd_flops() // 2,
+    }
+    exec_flops = {
+        "attn_fwd_kernel": w.fwd_flops(),
+        "attn_bwd_dkdv_kernel": 3 * w.fwd_flops(),
+        "attn_bwd_dq_kernel": 5 * w.fwd_flops() // 2,
+    }
+    kernels = {}
+    for name, t in per.items():
+        rec = {"ms": round(t, 4)}
+        if name in alg_flops and t > 0:
+            rec["alg_tflops"] = round(alg_flops[name] / (t * 1e-3) / 1e12, 1)
+            rec["exec_tflops"] = round(exec_flops[name] / (t * 1e-3) / 1e12, 1)
+        kernels[name] = rec
+    dominant = max(alg_flops, key=lambda n: per[n])
+    ach = alg_flops[dominant] / (per[dominant] * 1e-3) / 1e12
+    roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dominant, w.name)}
+    log(f"[bench] {K} steps: {ms_step:.4f} ms/step (events), wall {wall / K * 1e3:.4f} ms/step; "
+        f"kernels {kernels}")
+
+    out = {
+        "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak, causal S=4096 D=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
+                   "causal": True, "global_batch": w.B, "seq_len": w.S, "parallelism": "none"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(w.fwd_flops() / (per["attn_fwd_kernel"] * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(w.bwd_flops() / (sum(per[n] for n in per if "bwd" in n) * 1e-3) / 1e12, 1),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_groups)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

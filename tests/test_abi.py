@@ -1,0 +1,144 @@
+"""C ABI contract on the CPU: the library loads, exports what include/attn.h
+declares, and rejects every invalid argument before touching the GPU.
+
+Every call below fails validation, and validation happens before any HIP
+call, so none of them launches anything (no GPU is needed or used).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_attention_memory_amd as tam
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+A = 1 << 20          # fake, 16-byte aligned, far-apart "device" addresses (never dereferenced)
+GOOD = dict(B=1, Hq=4, Hkv=2, S=128, D=128, causal=1, scale=0.125)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(tam.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tam.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert tam.attn_version() == 1
+    for code in range(10):
+        assert tam.attn_status_string(code) and tam.attn_status_string(code) != "unknown status"
+    assert tam.attn_status_string(99) == "unknown status"
+
+
+def fwd(**kw):
+    args = dict(GOOD)
+    ptrs = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A)
+    for key in list(kw):
+        if key in ptrs:
+            ptrs[key] = kw.pop(key)
+    args.update(kw)
+    return tam.attn_fwd_raw(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], ptrs["lse"], args["B"],
+                            args["Hq"], args["Hkv"], args["S"], args["D"], args["causal"],
+                            args["scale"])
+
+
+def ws_bytes(**kw):
+    a = dict(GOOD, **kw)
+    return tam.attn_bwd_workspace_bytes(a["B"], a["Hq"], a["Hkv"], a["S"], a["D"])
+
+
+def bwd(ws_size=None, **kw):
+    args = dict(GOOD)
+    ptrs = dict(q=A, k=2 * A, v=3 * A, o=4 * A, dout=5 * A, lse=6 * A, dq=7 * A, dk=8 * A,
+                dv=9 * A, ws=10 * A)
+    for key in list(kw):
+        if key in ptrs:
+            ptrs[key] = kw.pop(key)
+    args.update(kw)
+    if ws_size is None:
+        ws_size = 0   # default: too small, so a fully valid call still cannot launch
+    return tam.attn_bwd_raw(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], ptrs["dout"], ptrs["lse"],
+                            ptrs["dq"], ptrs["dk"], ptrs["dv"], ptrs["ws"], ws_size, args["B"],
+                            args["Hq"], args["Hkv"], args["S"], args["D"], args["causal"],
+                            args["scale"])
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse"])
+def test_fwd_null_pointer(name):
+    assert fwd(**{name: 0}) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(S=0), 2), (dict(S=-5), 2),
+    (dict(Hq=6, Hkv=4), 2), (dict(S=(1 << 22) + 1), 2), (dict(B=1 << 20, Hq=1 << 5), 2),
+    (dict(D=96), 3), (dict(D=256), 3), (dict(D=0), 3),
+    (dict(scale=float("nan")), 4), (dict(scale=float("inf")), 4), (dict(scale=float("-inf")), 4),
+    (dict(causal=2), 8), (dict(causal=-1), 8),
+])
+def test_fwd_bad_arguments(kw, code):
+    assert fwd(**kw) == code
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse"])
+def test_fwd_misaligned(name):
+    base = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A)
+    assert fwd(**{name: base[name] + 8}) == 5
+
+
+def test_fwd_aliasing():
+    assert fwd(o=A) == 9                 # o on top of q
+    assert fwd(lse=4 * A + 64) == 9      # lse inside o
+    assert fwd(o=2 * A + 4096) == 9      # o overlapping k
+
+
+def test_workspace_query():
+    n = ws_bytes()
+    assert n >= 2 * 4 * 128 * 4           # Delta and scaled LSE, one float each per query row
+    assert n % 256 == 0
+    with pytest.raises(tam.AttnError):
+        ws_bytes(D=80)
+    with pytest.raises(tam.AttnError):
+        ws_bytes(Hq=3, Hkv=2)
+    lib = tam.load()
+    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 128, 128, None) == 1
+    # grows with the sequence; the longest workload still needs a modest workspace
+    assert ws_bytes(Hq=8, Hkv=1, S=81920) < 512 * 1024 * 1024
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"])
+def test_bwd_null_pointer(name):
+    assert bwd(**{name: 0}) == 1
+
+
+def test_bwd_workspace_checks():
+    need = ws_bytes()
+    assert bwd(ws_size=need - 1) == 6
+    assert bwd(ws=0, ws_size=need) == 6
+    assert bwd(ws=10 * A + 8, ws_size=need) == 5
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=5, Hkv=2), 2), (dict(D=32), 3), (dict(scale=float("nan")), 4), (dict(causal=3), 8),
+])
+def test_bwd_bad_arguments(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_aliasing():
+    need = ws_bytes()
+    assert bwd(ws_size=need, dq=A) == 9                    # dq on q
+    assert bwd(ws_size=need, dk=7 * A + 128) == 9          # dk inside dq
+    assert bwd(ws_size=need, ws=6 * A, ) == 9              # workspace on lse
+    assert bwd(ws_size=need, dv=5 * A) == 9                # dv on dout

@@ -1,0 +1,23 @@
+"""Exact causal GQA attention for MI355X (gfx950): HIP kernels behind a C ABI.
+
+The Python names mirror include/attn.h. The library is loaded on first use
+and every call fails loudly if it is missing; nothing here computes attention.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    STATUS,
+    BWD_EVENTS,
+    AttnError,
+    attn_bwd,
+    attn_bwd_raw,
+    attn_bwd_workspace_bytes,
+    attn_fwd,
+    attn_fwd_raw,
+    attn_status_string,
+    attn_version,
+    backward,
+    forward,
+    load,
+    workspace_for,
+)

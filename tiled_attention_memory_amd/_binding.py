@@ -1,0 +1,198 @@
+"""ctypes binding of libattn.so: argument marshalling only.
+
+Every computation happens in the HIP kernels behind the C ABI declared in
+include/attn.h. PyTorch is used only to own device memory and to provide the
+stream handle. There is no fallback: if the library is missing, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libattn.so")
+
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL_POINTER", 2: "ATTN_ERR_BAD_SHAPE",
+    3: "ATTN_ERR_UNSUPPORTED_HEAD_DIM", 4: "ATTN_ERR_BAD_SCALE", 5: "ATTN_ERR_MISALIGNED",
+    6: "ATTN_ERR_WORKSPACE", 7: "ATTN_ERR_HIP", 8: "ATTN_ERR_BAD_FLAG", 9: "ATTN_ERR_ALIAS",
+}
+
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_bwd_workspace_bytes", "attn_status_string",
+           "attn_version")
+BWD_EVENTS = 5
+
+_lock = threading.Lock()
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({attn_status_string(status)})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libattn.so (built in-tree by tiled_attention_memory_amd.build)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m tiled_attention_memory_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        lib.attn_fwd.restype = i
+        lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                 i, i, i, i, i, i, f, vp]
+        lib.attn_bwd.restype = i
+        lib.attn_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                       i, i, i, i, i, i, f, vp, vp]
+        lib.attn_bwd_timed.restype = i
+        lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, ctypes.POINTER(sz)]
+        lib.attn_bwd_workspace_bytes.restype = i
+        lib.attn_status_string.argtypes = [i]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_version.argtypes = []
+        lib.attn_version.restype = i
+        _lib = lib
+        return lib
+
+
+def attn_status_string(status: int) -> str:
+    return load().attn_status_string(int(status)).decode()
+
+
+def attn_version() -> int:
+    return load().attn_version()
+
+
+# ---------------------------------------------------------------------------
+# raw entry points: plain integers for pointers (used for the C ABI contract)
+# ---------------------------------------------------------------------------
+def attn_fwd_raw(q, k, v, o, lse, B, Hq, Hkv, S, D, causal, scale, stream=0) -> int:
+    return load().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, S, D, int(causal), float(scale), stream)
+
+
+def attn_bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, S, D, causal,
+                 scale, stream=0) -> int:
+    return load().attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, S, D,
+                           int(causal), float(scale), stream)
+
+
+def attn_bwd_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, D: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = load().attn_bwd_workspace_bytes(B, Hq, Hkv, S, D, ctypes.byref(out))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_workspace_bytes")
+    return out.value
+
+
+# ---------------------------------------------------------------------------
+# torch-tensor entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def _shape(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, S, D]")
+    B, Hq, S, D = q.shape
+    if k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q shape {tuple(q.shape)}")
+    return B, Hq, k.shape[1], S, D
+
+
+def _check(t, name, dtype, shape):
+    import torch
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _scale(scale, D):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def attn_fwd(q, k, v, o, lse, causal=True, scale=None, stream=None) -> None:
+    """Enqueue the forward pass: writes o (bf16) and lse (fp32) in place."""
+    import torch
+    B, Hq, Hkv, S, D = _shape(q, k)
+    bf = torch.bfloat16
+    p = [_check(q, "q", bf, (B, Hq, S, D)), _check(k, "k", bf, (B, Hkv, S, D)),
+         _check(v, "v", bf, (B, Hkv, S, D)), _check(o, "o", bf, (B, Hq, S, D)),
+         _check(lse, "lse", torch.float32, (B, Hq, S))]
+    st = load().attn_fwd(*p, B, Hq, Hkv, S, D, int(bool(causal)), _scale(scale, D), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal=True, scale=None,
+             stream=None, events=None) -> None:
+    """Enqueue the backward pass: writes dq, dk, dv (bf16) in place.
+
+    events: optional ctypes array of BWD_EVENTS hipEvent_t handles; when given,
+    the call goes through attn_bwd_timed and records them between the kernels.
+    """
+    import torch
+    B, Hq, Hkv, S, D = _shape(q, k)
+    bf = torch.bfloat16
+    p = [_check(q, "q", bf, (B, Hq, S, D)), _check(k, "k", bf, (B, Hkv, S, D)),
+         _check(v, "v", bf, (B, Hkv, S, D)), _check(o, "o", bf, (B, Hq, S, D)),
+         _check(dout, "dout", bf, (B, Hq, S, D)), _check(lse, "lse", torch.float32, (B, Hq, S)),
+         _check(dq, "dq", bf, (B, Hq, S, D)), _check(dk, "dk", bf, (B, Hkv, S, D)),
+         _check(dv, "dv", bf, (B, Hkv, S, D))]
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    args = (*p, workspace.data_ptr(), workspace.numel(), B, Hq, Hkv, S, D, int(bool(causal)),
+            _scale(scale, D), _stream(stream))
+    if events is None:
+        st = load().attn_bwd(*args)
+    else:
+        st = load().attn_bwd_timed(*args, ctypes.cast(events, ctypes.c_void_p))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+
+
+# ---------------------------------------------------------------------------
+# conveniences that allocate outputs with torch, then call the entry points
+# ---------------------------------------------------------------------------
+def forward(q, k, v, causal=True, scale=None, stream=None):
+    import torch
+    B, Hq, Hkv, S, D = _shape(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, causal, scale, stream)
+    return o, lse
+
+
+def workspace_for(q, k):
+    import torch
+    B, Hq, Hkv, S, D = _shape(q, k)
+    return torch.empty(attn_bwd_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8,
+                       device=q.device)
+
+
+def backward(q, k, v, o, dout, lse, causal=True, scale=None, stream=None, workspace=None):
+    import torch
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = workspace_for(q, k) if workspace is None else workspace
+    attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, causal, scale, stream)
+    return dq, dk, dv

@@ -1,0 +1,657 @@
+// Backward pass of exact attention for gfx950.
+//
+// Follows the "Recomputation" bullet of the page "使用 PyTorch FSDP 微調 Llama 2 70B"
+// (agentlenshq.com), section "Flash Attention": the probabilities are
+// recomputed tile by tile from Q, K and the forward pass's log-sum-exp
+// instead of being stored, so no N x N matrix is ever written.
+//
+// With P = exp(s - LSE), L = sum(O * dO):
+//   dV = P^T dO,  dP = dO V^T,  Delta_i = sum_d dO_id O_id,
+//   dS = P * (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Kernels, all on the caller's stream:
+//   1. prep:  Delta~ = sum_d dO_id O_id from the stored bf16 O, and
+//             LSE * log2(e), per query row (workspace).
+//   2. dq:    query-stationary, like the forward pass: dQ^T += K^T dS^T. It also
+//             makes Delta exact: with dS~ = P (dP - Delta~) and sum_j P_ij = 1,
+//             Delta_i - Delta~_i = sum_j dS~_ij =: c_i, so
+//             dQ_i = scale (sum_j dS~_ij K_j - c_i sum_j P_ij K_j), and the exact
+//             Delta_i = Delta~_i + c_i is written back for kernel 3. This removes
+//             the error that rounding O to bf16 puts into Delta.
+//   3. dkdv:  key-stationary. One unit = (batch, kv head, 128-key tile, subset
+//             of the group's query heads); 4 waves own 32 keys each and keep
+//             K, V (as MFMA operands) and the dK^T, dV^T accumulators in
+//             registers while 64-row Q/dO tiles stream through LDS. No
+//             atomics: each unit owns its output rows; with more than one
+//             head subset, fp32 partials go to the workspace.
+//   4. reduce (only with several subsets): sums the partials in a fixed order.
+// The second operand of every gradient product (P for dV, dS for dK and dQ)
+// enters the bf16 MFMA as a hi + lo pair of bf16 values, so those products
+// carry about 16 significant bits of P and dS instead of 8.
+// Every output element is produced by one thread in a fixed order, so the
+// results are bitwise reproducible.
+#include <math.h>
+
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace tam {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kQBR = 128;   // dq: query rows per workgroup
+constexpr int kQBC = 64;    // dq: keys per tile
+constexpr int kKBC = 128;   // dkdv: keys per workgroup
+constexpr int kKBR = 64;    // dkdv: query rows per streamed tile
+constexpr int kTargetUnits = 1024;
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int choose_head_split(const AttnShape& sh) {
+  const int g = sh.Hq / sh.Hkv;
+  const long long units = (long long)sh.B * sh.Hkv * ((sh.S + kKBC - 1) / kKBC);
+  int ns = 1;
+  while (units * ns < kTargetUnits && ns < g) {
+    int next = ns + 1;
+    while (g % next) ++next;
+    ns = next;
+  }
+  return ns;
+}
+
+struct WsLayout {
+  size_t delta, lse2, part, total;
+  int nsplit;
+};
+
+WsLayout ws_layout(const AttnShape& sh) {
+  WsLayout w;
+  const size_t rows = (size_t)sh.B * sh.Hq * sh.S;
+  w.nsplit = choose_head_split(sh);
+  w.delta = 0;
+  w.lse2 = align256(rows * 4);
+  w.part = w.lse2 + align256(rows * 4);
+  const size_t kv_elems = (size_t)sh.B * sh.Hkv * sh.S * sh.D;
+  w.total = w.part + (w.nsplit > 1 ? align256((size_t)w.nsplit * 2 * kv_elems * 4) : 0);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// 1. prep: Delta_i = sum_d dO_id * O_id, lse2_i = LSE_i * log2(e)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(const uint16_t* o, const uint16_t* dout,
+                                                                 const float* lse, float* delta,
+                                                                 float* lse2, long long rows) {
+  constexpr int TPR = D / 8;         // threads per row, 8 elements each
+  constexpr int RPB = kThreads / TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(o + row * D + part * 8);
+    const u32x4 dv = *reinterpret_cast<const u32x4*>(dout + row * D + part * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(bf16_lo(ov[w]), bf16_lo(dv[w]), acc);
+      acc = fmaf(bf16_hi(ov[w]), bf16_hi(dv[w]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK/dV, key-stationary
+// ---------------------------------------------------------------------------
+struct DkdvArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* delta;
+  const float* lse2;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* part;  // [nsplit][2][B*Hkv*S*D] fp32 partials when nsplit > 1
+  int Hq, Hkv, S, nsplit;
+  float c;      // scale * log2(e)
+  float scale;
+  TileSched sched;  // streams = (batch*Hkv + kv head) * nsplit + subset; tiles = key tiles
+};
+
+template <int D>
+struct DkdvLds {
+  static constexpr int STR = D + 8;
+  static constexpr int QT = kKBR * STR;       // Q tile
+  static constexpr int DOT = kKBR * STR;      // dO tile
+  static constexpr int STAGE = QT + DOT + 2 * kKBR * 2;  // + lse2, delta as fp32 (2 uint16 each)
+  static constexpr int ELEMS = 2 * STAGE;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(DkdvArgs a) {
+  using L = DkdvLds<D>;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int NCH = kKBR * CPR / kThreads;
+  static_assert(NCH * kThreads == kKBR * CPR, "tile must split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+
+  int stream, t;
+  if (!sched_decode(a.sched, blockIdx.x, &stream, &t)) return;
+  const int jt = a.sched.NT - 1 - t;  // key tile; ascending = heaviest first when causal
+  const int grp = stream / a.nsplit, sub = stream - grp * a.nsplit;
+  const int b = grp / a.Hkv, kvh = grp - b * a.Hkv;
+  const int g = a.Hq / a.Hkv;
+  const int hps = g / a.nsplit;           // query heads per subset
+  const int h_first = kvh * g + sub * hps;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int S = a.S;
+  const size_t kv_base = (size_t)grp * S * D;
+  const int kvt0 = jt * kKBC;
+  const int kvb0 = kvt0 + 32 * wave;   // this wave's first key
+  const int kvrow = kvb0 + col;        // the key this lane owns
+
+  // K and V rows as MFMA B operands, resident for the whole unit.
+  bf16x8 kf[KS], vf[KS];
+  {
+    const size_t off = kv_base + (size_t)kvrow * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bool in = kvrow < S;
+      kf[ks] = in ? *reinterpret_cast<const bf16x8*>(a.k + off + 16 * ks)
+                  : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+      vf[ks] = in ? *reinterpret_cast<const bf16x8*>(a.v + off + 16 * ks)
+                  : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
+  }
+
+  const int NQ = (S + kKBR - 1) / kKBR;
+  const int i_min = CAUSAL ? kvt0 / kKBR : 0;
+  const int per_head = NQ - i_min;       // query tiles visited per head
+  const int nsteps = per_head * hps;
+
+  // step -> (query head, query tile); tiles run from the last one down so that
+  // concurrent units of one group read the same Q/dO tiles at the same time.
+  auto step_head = [&](int st) { return h_first + st / per_head; };
+  auto step_tile = [&](int st) { return NQ - 1 - st % per_head; };
+
+  u32x4 qreg[NCH], dreg[NCH];
+  float fl = 0.f;
+  auto gload = [&](int st) {
+    const int hq = step_head(st), it = step_tile(st);
+    const size_t qb = ((size_t)b * a.Hq + hq) * S * D;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cidx = tid + kThreads * i;
+      const int r = cidx / CPR, cc = cidx % CPR;
+      const int row = it * kKBR + r;
+      if (row < S) {
+        const size_t off = qb + (size_t)row * D + cc * 8;
+        qreg[i] = *reinterpret_cast<const u32x4*>(a.q + off);
+        dreg[i] = *reinterpret_cast<const u32x4*>(a.dout + off);
+      } else {
+        qreg[i] = u32x4{0, 0, 0, 0};
+        dreg[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < 2 * kKBR) {
+      const int r = tid & (kKBR - 1);
+      const int row = it * kKBR + r;
+      const size_t ro = ((size_t)b * a.Hq + hq) * S + row;
+      fl = row < S ? (tid < kKBR ? a.lse2[ro] : a.delta[ro]) : 0.f;
+    }
+  };
+  auto lstore = [&](int stage) {
+    uint16_t* qs_ = smem + stage * L::STAGE;
+    uint16_t* ds_ = qs_ + L::QT;
+    float* fs_ = reinterpret_cast<float*>(ds_ + L::DOT);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cidx = tid + kThreads * i;
+      const int r = cidx / CPR, cc = cidx % CPR;
+      *reinterpret_cast<u32x4*>(qs_ + r * L::STR + cc * 8) = qreg[i];
+      *reinterpret_cast<u32x4*>(ds_ + r * L::STR + cc * 8) = dreg[i];
+    }
+    if (tid < 2 * kKBR) fs_[tid] = fl;  // [0, 64) lse2, [64, 128) delta
+  };
+
+  f32x16 acck[DB], accv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    acck[db] = f32x16{};
+    accv[db] = f32x16{};
+  }
+  const float c = a.c;
+  const int i16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1);
+
+  if (nsteps > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int stage = st & 1;
+    if (st + 1 < nsteps) gload(st + 1);
+    const int it = step_tile(st);
+    const uint16_t* Qs = smem + stage * L::STAGE;
+    const uint16_t* Ds = Qs + L::QT;
+    const float* Fs = reinterpret_cast<const float*>(Ds + L::DOT);
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int qb0 = it * kKBR + qs * 32;   // first query row of this sub-block
+      if (CAUSAL && qb0 + 31 < kvb0) continue;  // every row is before every key of this wave
+      // S[q][kv] and dP[q][kv]: lane holds key kvrow, rows qb0 + 8(v/4) + 4half + v%4
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const uint16_t* qp = Qs + (qs * 32 + col) * L::STR + 8 * half;
+      const uint16_t* dp_ = Ds + (qs * 32 + col) * L::STR + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(lds_read_b128(qp + 16 * ks), kf[ks], s);
+        dp = mfma32(lds_read_b128(dp_ + 16 * ks), vf[ks], dp);
+      }
+      const bool masked = (CAUSAL && qb0 < kvb0 + 31) || qb0 + 32 > S || kvb0 + 32 > S;
+      float p[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ql = qs * 32 + 8 * i + 4 * half;   // local row of v = 4i
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(Fs + ql);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(Fs + kKBR + ql);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = 4 * i + r;
+          float e = fast_exp2(fmaf(s[v], c, -l2[r]));
+          if (masked) {
+            const int qrow = it * kKBR + ql + r;
+            const bool ok = qrow < S && kvrow < S && (!CAUSAL || kvrow <= qrow);
+            e = ok ? e : 0.f;
+          }
+          p[v] = e;
+          ds[v] = e * (dp[v] - dl[r]);
+        }
+      }
+      bf16x8 ph[2], pl[2], dh[2], dl[2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        split_bf16x8(p + 8 * k2, &ph[k2], &pl[k2]);
+        split_bf16x8(ds + 8 * k2, &dh[k2], &dl[k2]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS; A operands read transposed from the row-major tiles.
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int roff = (qs * 32 + k2 * 16 + 4 * half + (i16 >> 2)) * L::STR + db * 32 + dsub + 4 * (i16 & 3);
+          const bf16x8 a_do = lds_read_tr_pair(Ds + roff, Ds + roff + 8 * L::STR);
+          const bf16x8 a_q = lds_read_tr_pair(Qs + roff, Qs + roff + 8 * L::STR);
+          accv[db] = mfma32(a_do, ph[k2], accv[db]);
+          accv[db] = mfma32(a_do, pl[k2], accv[db]);
+          acck[db] = mfma32(a_q, dh[k2], acck[db]);
+          acck[db] = mfma32(a_q, dl[k2], acck[db]);
+        }
+    }
+    if (st + 1 < nsteps) lstore(stage ^ 1);
+    __syncthreads();
+  }
+
+  // lane holds key kvrow, head-dim entries 32db + 8i + 4half + (0..3)
+  if (kvrow < S) {
+    if (a.nsplit == 1) {
+      uint16_t* kp = a.dk + kv_base + (size_t)kvrow * D + 4 * half;
+      uint16_t* vp = a.dv + kv_base + (size_t)kvrow * D + 4 * half;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x16& K = acck[db];
+          const f32x16& V = accv[db];
+          u32x2 wk = {pack_bf16(K[4 * i] * a.scale, K[4 * i + 1] * a.scale),
+                      pack_bf16(K[4 * i + 2] * a.scale, K[4 * i + 3] * a.scale)};
+          u32x2 wv = {pack_bf16(V[4 * i], V[4 * i + 1]), pack_bf16(V[4 * i + 2], V[4 * i + 3])};
+          *reinterpret_cast<u32x2*>(kp + 32 * db + 8 * i) = wk;
+          *reinterpret_cast<u32x2*>(vp + 32 * db + 8 * i) = wv;
+        }
+    } else {
+      const size_t total = (size_t)(a.sched.BH / a.nsplit) * S * D;  // B*Hkv*S*D
+      float* kp = a.part + ((size_t)sub * 2) * total + kv_base + (size_t)kvrow * D + 4 * half;
+      float* vp = kp + total;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x16& K = acck[db];
+          const f32x16& V = accv[db];
+          f32x4 wk = {K[4 * i] * a.scale, K[4 * i + 1] * a.scale, K[4 * i + 2] * a.scale,
+                      K[4 * i + 3] * a.scale};
+          f32x4 wv = {V[4 * i], V[4 * i + 1], V[4 * i + 2], V[4 * i + 3]};
+          *reinterpret_cast<f32x4*>(kp + 32 * db + 8 * i) = wk;
+          *reinterpret_cast<f32x4*>(vp + 32 * db + 8 * i) = wv;
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. fixed-order sum of the per-subset partials -> bf16 dK, dV
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void attn_bwd_reduce_kernel(const float* part, uint16_t* dk,
+                                                                   uint16_t* dv, long long n4,
+                                                                   int nsplit) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;  // index of a 4-element group
+  if (i >= n4) return;
+  const size_t total = (size_t)n4 * 4;
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    sk += *reinterpret_cast<const f32x4*>(part + (size_t)s * 2 * total + (size_t)i * 4);
+    sv += *reinterpret_cast<const f32x4*>(part + ((size_t)s * 2 + 1) * total + (size_t)i * 4);
+  }
+  *reinterpret_cast<u32x2*>(dk + (size_t)i * 4) = u32x2{pack_bf16(sk[0], sk[1]), pack_bf16(sk[2], sk[3])};
+  *reinterpret_cast<u32x2*>(dv + (size_t)i * 4) = u32x2{pack_bf16(sv[0], sv[1]), pack_bf16(sv[2], sv[3])};
+}
+
+// ---------------------------------------------------------------------------
+// 4. dQ, query-stationary
+// ---------------------------------------------------------------------------
+struct DqArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  float* delta;  // in: Delta~ from the stored O; out: exact Delta
+  const float* lse2;
+  uint16_t* dq;
+  int Hq, Hkv, S;
+  float c;
+  float scale;
+  TileSched sched;
+};
+
+template <int D>
+struct DqLds {
+  static constexpr int KSTR = D + 8;
+  static constexpr int VSTR = D + 8;
+  static constexpr int KTILE = kQBC * KSTR;
+  static constexpr int VTILE = kQBC * VSTR;
+  static constexpr int STAGE = KTILE + VTILE;
+  static constexpr int ELEMS = 2 * STAGE;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dq_kernel(DqArgs a) {
+  using L = DqLds<D>;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int NCH = kQBC * CPR / kThreads;
+  static_assert(NCH * kThreads == kQBC * CPR, "tile must split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+
+  int bh, qt;
+  if (!sched_decode(a.sched, blockIdx.x, &bh, &qt)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int S = a.S;
+  const int b = bh / a.Hq, h = bh - b * a.Hq;
+  const int kvh = h / (a.Hq / a.Hkv);
+  const size_t q_base = (size_t)bh * S * D;
+  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
+  const int q0 = qt * kQBR;
+  const int wrow0 = q0 + wave * 32;
+  const int qrow = wrow0 + col;
+
+  bf16x8 qf[KS], df[KS];
+  {
+    const size_t off = q_base + (size_t)qrow * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bool in = qrow < S;
+      qf[ks] = in ? *reinterpret_cast<const bf16x8*>(a.q + off + 16 * ks)
+                  : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+      df[ks] = in ? *reinterpret_cast<const bf16x8*>(a.dout + off + 16 * ks)
+                  : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
+  }
+  const float l2row = qrow < S ? a.lse2[(size_t)bh * S + qrow] : 0.f;
+  const float drow = qrow < S ? a.delta[(size_t)bh * S + qrow] : 0.f;
+
+  const int last_row = min(q0 + kQBR, S) - 1;
+  const int n_kv = (S + kQBC - 1) / kQBC;
+  const int ntiles = CAUSAL ? min(n_kv, last_row / kQBC + 1) : n_kv;
+
+  u32x4 kreg[NCH], vreg[NCH];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cidx = tid + kThreads * i;
+      const int r = cidx / CPR, cc = cidx % CPR;
+      const int row = j * kQBC + r;
+      if (row < S) {
+        const size_t off = kv_base + (size_t)row * D + cc * 8;
+        kreg[i] = *reinterpret_cast<const u32x4*>(a.k + off);
+        vreg[i] = *reinterpret_cast<const u32x4*>(a.v + off);
+      } else {
+        kreg[i] = u32x4{0, 0, 0, 0};
+        vreg[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&](int stage) {
+    uint16_t* ks_ = smem + stage * L::STAGE;
+    uint16_t* vs_ = ks_ + L::KTILE;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cidx = tid + kThreads * i;
+      const int r = cidx / CPR, cc = cidx % CPR;
+      *reinterpret_cast<u32x4*>(ks_ + r * L::KSTR + cc * 8) = kreg[i];
+      *reinterpret_cast<u32x4*>(vs_ + r * L::VSTR + cc * 8) = vreg[i];
+    }
+  };
+
+  f32x16 acc[DB], accpk[DB];  // dQ^T with Delta~, and (P K)^T for the exact-Delta correction
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    acc[db] = f32x16{};
+    accpk[db] = f32x16{};
+  }
+  float csum = 0.f;  // this lane's half of c = sum_j dS~_j for its row
+  const float c = a.c;
+  const int i16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1);
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int stage = j & 1;
+    if (j + 1 < ntiles) gload(j + 1);
+    const int kv0 = j * kQBC;
+    const bool active = !CAUSAL || kv0 <= wrow0 + 31;
+    if (active) {
+      const uint16_t* Ks = smem + stage * L::STAGE;
+      const uint16_t* Vs = Ks + L::KTILE;
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+        const uint16_t* kp = Ks + (kb * 32 + col) * L::KSTR + 8 * half;
+        const uint16_t* vp = Vs + (kb * 32 + col) * L::VSTR + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s[kb] = mfma32(lds_read_b128(kp + 16 * ks), qf[ks], s[kb]);
+          dp[kb] = mfma32(lds_read_b128(vp + 16 * ks), df[ks], dp[kb]);
+        }
+      }
+      const bool masked = (kv0 + kQBC > S) || (CAUSAL && kv0 + kQBC - 1 > wrow0);
+      bf16x8 dh[2][2], dl[2][2], ph[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float ds[16], pf[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float e = fast_exp2(fmaf(s[kb][v], c, -l2row));
+          if (masked) {
+            const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+            const bool ok = kv < S && (!CAUSAL || kv <= qrow);
+            e = ok ? e : 0.f;
+          }
+          pf[v] = e;
+          ds[v] = e * (dp[kb][v] - drow);
+          csum += ds[v];
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          split_bf16x8(ds + 8 * k2, &dh[kb][k2], &dl[kb][k2]);
+          ph[kb][k2] = pack_bf16x8(pf + 8 * k2);
+        }
+      }
+      // dQ^T += K^T dS~^T (hi and lo parts) and (PK)^T += K^T P^T: K read transposed
+      // from its row-major tile once for all three products.
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const uint16_t* kp =
+                Ks + (kb * 32 + k2 * 16 + 4 * half + (i16 >> 2)) * L::KSTR + db * 32 + dsub + 4 * (i16 & 3);
+            const bf16x8 a_k = lds_read_tr_pair(kp, kp + 8 * L::KSTR);
+            acc[db] = mfma32(a_k, dh[kb][k2], acc[db]);
+            acc[db] = mfma32(a_k, dl[kb][k2], acc[db]);
+            accpk[db] = mfma32(a_k, ph[kb][k2], accpk[db]);
+          }
+    }
+    if (j + 1 < ntiles) lstore(stage ^ 1);
+    __syncthreads();
+  }
+
+  const float corr = sum_halves(csum);  // Delta_i - Delta~_i
+  if (qrow < S) {
+    uint16_t* op = a.dq + q_base + (size_t)qrow * D + 4 * half;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float g[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) g[r] = a.scale * fmaf(-corr, accpk[db][4 * i + r], acc[db][4 * i + r]);
+        u32x2 w = {pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3])};
+        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i) = w;
+      }
+    if (half == 0) a.delta[(size_t)bh * S + qrow] = drow + corr;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+hipError_t launch_all(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* o, const uint16_t* dout, const float* lse, uint16_t* dq,
+                      uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t stream,
+                      hipEvent_t* ev) {
+  const WsLayout w = ws_layout(sh);
+  char* ws = static_cast<char*>(workspace);
+  float* delta = reinterpret_cast<float*>(ws + w.delta);
+  float* lse2 = reinterpret_cast<float*>(ws + w.lse2);
+  float* part = reinterpret_cast<float*>(ws + w.part);
+  const float c = sh.scale * kLog2e;
+  hipError_t e;
+  auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  if ((e = mark(0)) != hipSuccess) return e;
+
+  {  // 1. prep
+    const long long rows = (long long)sh.B * sh.Hq * sh.S;
+    constexpr int RPB = kThreads / (D / 8);
+    const long long grid = (rows + RPB - 1) / RPB;
+    void* args[] = {(void*)&o, (void*)&dout, (void*)&lse, (void*)&delta, (void*)&lse2, (void*)&rows};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_prep_kernel<D>), dim3((unsigned)grid),
+                        dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess || (e = mark(1)) != hipSuccess) return e;
+  }
+  {  // 2. dQ (also turns Delta~ into the exact Delta)
+    DqArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.delta = delta;
+    a.lse2 = lse2;
+    a.dq = dq;
+    a.Hq = sh.Hq;
+    a.Hkv = sh.Hkv;
+    a.S = sh.S;
+    a.c = c;
+    a.scale = sh.scale;
+    a.sched.BH = sh.B * sh.Hq;
+    a.sched.NT = (sh.S + kQBR - 1) / kQBR;
+    a.sched.chunk = (a.sched.BH + 7) / 8;
+    void* args[] = {&a};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL>),
+                        dim3((unsigned)sched_grid(a.sched)), dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess || (e = mark(2)) != hipSuccess) return e;
+  }
+  {  // 3. dK/dV
+    DkdvArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.delta = delta;
+    a.lse2 = lse2;
+    a.dk = dk;
+    a.dv = dv;
+    a.part = part;
+    a.Hq = sh.Hq;
+    a.Hkv = sh.Hkv;
+    a.S = sh.S;
+    a.nsplit = w.nsplit;
+    a.c = c;
+    a.scale = sh.scale;
+    a.sched.BH = sh.B * sh.Hkv * w.nsplit;
+    a.sched.NT = (sh.S + kKBC - 1) / kKBC;
+    a.sched.chunk = (a.sched.BH + 7) / 8;
+    void* args[] = {&a};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL>),
+                        dim3((unsigned)sched_grid(a.sched)), dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess || (e = mark(3)) != hipSuccess) return e;
+  }
+  if (w.nsplit > 1) {  // 4. fixed-order sum of the head-subset partials
+    const long long n4 = (long long)sh.B * sh.Hkv * sh.S * sh.D / 4;
+    const long long grid = (n4 + kThreads - 1) / kThreads;
+    int ns = w.nsplit;
+    void* args[] = {(void*)&part, (void*)&dk, (void*)&dv, (void*)&n4, (void*)&ns};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_reduce_kernel), dim3((unsigned)grid),
+                        dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  return mark(4);
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(const AttnShape& sh) { return ws_layout(sh).total; }
+
+hipError_t launch_bwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* o, const uint16_t* dout, const float* lse, uint16_t* dq,
+                      uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t stream,
+                      hipEvent_t* ev) {
+  if (sh.D == 128)
+    return sh.causal ? launch_all<128, true>(sh, q, k, v, o, dout, lse, dq, dk, dv, workspace, stream, ev)
+                     : launch_all<128, false>(sh, q, k, v, o, dout, lse, dq, dk, dv, workspace, stream, ev);
+  return sh.causal ? launch_all<64, true>(sh, q, k, v, o, dout, lse, dq, dk, dv, workspace, stream, ev)
+                   : launch_all<64, false>(sh, q, k, v, o, dout, lse, dq, dk, dv, workspace, stream, ev);
+}
+
+}  // namespace tam

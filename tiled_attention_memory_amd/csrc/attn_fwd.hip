@@ -1,0 +1,279 @@
+// Forward pass of exact attention for gfx950: one fused kernel.
+//
+// Follows the page "使用 PyTorch FSDP 微調 Llama 2 70B" (agentlenshq.com),
+// section "Flash Attention": the score matrix is processed in tiles that stay
+// on chip ("Tiling"), normalised with an online softmax, and fused with both
+// products so that only O and one log-sum-exp per row are written to HBM
+// ("Kernel Fusion").
+//
+// Work unit: one (batch, query head, 128-row query tile); 4 waves, each owning
+// 32 query rows. Per 64-key tile:
+//   S^T = K Q^T       (MFMA; A = K rows from LDS, B = Q rows held in registers)
+//   online softmax    (each lane owns one query row: its running max, its
+//                      partial row sum and its output column rescale are
+//                      per-lane scalars; one cross-half exchange per tile)
+//   O^T += V^T P^T    (MFMA; A = V read transposed from LDS, B = P straight
+//                      from the S^T accumulator after bf16 rounding)
+// K/V tiles are staged through double-buffered LDS by all 256 threads with
+// coalesced 16-byte loads; the next tile's loads are in flight while the
+// current one is consumed. Under a causal mask, key tiles past the diagonal
+// are never visited and only tiles that straddle it evaluate the mask.
+#include <math.h>
+
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace tam {
+namespace {
+
+constexpr int kBR = 128;      // query rows per workgroup
+constexpr int kBC = 64;       // keys per tile
+constexpr int kThreads = 256;
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int Hq, Hkv, S;
+  float c;  // softmax scale * log2(e): scores are exponentiated in base 2
+  TileSched sched;
+};
+
+template <int D>
+struct FwdLds {
+  static constexpr int KSTR = D + 8;    // K rows: 16-byte reads along a row, conflict-free with +16 B pad
+  static constexpr int VSTR = D + 16;   // V rows: transposed 4x16 block reads, +32 B pad
+  static constexpr int KTILE = kBC * KSTR;
+  static constexpr int VTILE = kBC * VSTR;
+  static constexpr int STAGE = KTILE + VTILE;
+  static constexpr int ELEMS = 2 * STAGE;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
+  using L = FwdLds<D>;
+  constexpr int KS = D / 16;                  // MFMA k-steps over the head dimension
+  constexpr int DB = D / 32;                  // 32-row blocks of the O^T accumulator
+  constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
+  constexpr int NCH = kBC * CPR / kThreads;   // chunks per thread per tensor per tile
+  static_assert(NCH * kThreads == kBC * CPR, "tile must split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+
+  int bh, qt;
+  if (!sched_decode(a.sched, blockIdx.x, &bh, &qt)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int S = a.S;
+  const int b = bh / a.Hq, h = bh - b * a.Hq;
+  const int kvh = h / (a.Hq / a.Hkv);
+  const size_t q_base = (size_t)bh * S * D;
+  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
+  const int q0 = qt * kBR;
+  const int wrow0 = q0 + wave * 32;  // first query row of this wave
+  const int qrow = wrow0 + col;      // the query row this lane owns
+
+  // Q rows as MFMA B operands (k = head dim), resident for the whole loop.
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = a.q + q_base + (size_t)qrow * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = qrow < S ? *reinterpret_cast<const bf16x8*>(qp + 16 * ks)
+                        : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
+
+  const int last_row = min(q0 + kBR, S) - 1;
+  const int n_kv = (S + kBC - 1) / kBC;
+  const int ntiles = CAUSAL ? min(n_kv, last_row / kBC + 1) : n_kv;
+
+  u32x4 kreg[NCH], vreg[NCH];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cidx = tid + kThreads * i;
+      const int r = cidx / CPR, cc = cidx % CPR;
+      const int row = j * kBC + r;
+      if (row < S) {
+        const size_t off = kv_base + (size_t)row * D + cc * 8;
+        kreg[i] = *reinterpret_cast<const u32x4*>(a.k + off);
+        vreg[i] = *reinterpret_cast<const u32x4*>(a.v + off);
+      } else {
+        kreg[i] = u32x4{0, 0, 0, 0};
+        vreg[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&](int stage) {
+    uint16_t* ks_ = smem + stage * L::STAGE;
+    uint16_t* vs_ = ks_ + L::KTILE;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cidx = tid + kThreads * i;
+      const int r = cidx / CPR, cc = cidx % CPR;
+      *reinterpret_cast<u32x4*>(ks_ + r * L::KSTR + cc * 8) = kreg[i];
+      *reinterpret_cast<u32x4*>(vs_ + r * L::VSTR + cc * 8) = vreg[i];
+    }
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY;  // running max of this row's base-2 scaled scores
+  float l_run = 0.f;        // running sum of this lane's half of the row
+  const float c = a.c;
+  const bool c_nonneg = c >= 0.f;
+  const float fill = c_nonneg ? -INFINITY : INFINITY;  // masked score: never the extreme
+
+  // transposed-read coordinates of this lane inside its 16-lane group
+  const int i16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1);
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int stage = j & 1;
+    if (j + 1 < ntiles) gload(j + 1);
+    const int kv0 = j * kBC;
+    const bool active = !CAUSAL || kv0 <= wrow0 + 31;
+    if (active) {
+      const uint16_t* Ks = smem + stage * L::STAGE;
+      const uint16_t* Vs = Ks + L::KTILE;
+
+      // S^T for two 32-key blocks: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow.
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        const uint16_t* kp = Ks + (kb * 32 + col) * L::KSTR + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s[kb] = mfma32(lds_read_b128(kp + 16 * ks), qf[ks], s[kb]);
+      }
+
+      const bool masked = (kv0 + kBC > S) || (CAUSAL && kv0 + kBC - 1 > wrow0);
+      if (masked) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+            const bool ok = kv < S && (!CAUSAL || kv <= qrow);
+            if (!ok) s[kb][v] = fill;
+          }
+      }
+
+      // row extreme of the raw scores (max if the scale is >= 0, else min)
+      float ext = s[0][0];
+      if (c_nonneg) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) ext = fmaxf(ext, s[kb][v]);
+        ext = max_halves(ext);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) ext = fminf(ext, s[kb][v]);
+        ext = min_halves(ext);
+      }
+      // A tile where all of this row's keys are masked gives NaN (c == 0) or -inf
+      // here; fmaxf keeps the running max in both cases.
+      const float m_new = fmaxf(m_run, ext * c);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+
+      float p[2][16];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float e = fast_exp2(fmaf(s[kb][v], c, -m_new));
+          if (masked) {
+            const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+            const bool ok = kv < S && (!CAUSAL || kv <= qrow);
+            e = ok ? e : 0.f;
+          }
+          p[kb][v] = e;
+          lsum += e;
+        }
+      l_run = fmaf(l_run, alpha, lsum);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) pb[kb][k2] = pack_bf16x8(&p[kb][8 * k2]);
+
+      // O^T += V^T P^T: the k index of MFMA (kb, k2) slot t of lane half hh is key
+      // 32kb + 16k2 + 8(t/4) + 4hh + t%4, matching where P sits in the S^T accumulator.
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const uint16_t* vp =
+                Vs + (kb * 32 + k2 * 16 + 4 * half + (i16 >> 2)) * L::VSTR + db * 32 + dsub + 4 * (i16 & 3);
+            acc[db] = mfma32(lds_read_tr_pair(vp, vp + 8 * L::VSTR), pb[kb][k2], acc[db]);
+          }
+    }
+    if (j + 1 < ntiles) lstore(stage ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = sum_halves(l_run);
+  if (qrow < S) {
+    const float inv = 1.f / l_tot;
+    uint16_t* op = a.o + q_base + (size_t)qrow * D + 4 * half;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 w = {pack_bf16(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv),
+                   pack_bf16(acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i) = w;
+      }
+    if (half == 0) a.lse[(size_t)bh * S + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  uint16_t* o, float* lse, hipStream_t stream) {
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.Hq = sh.Hq;
+  a.Hkv = sh.Hkv;
+  a.S = sh.S;
+  a.c = sh.scale * kLog2e;
+  a.sched.BH = sh.B * sh.Hq;
+  a.sched.NT = (sh.S + kBR - 1) / kBR;
+  a.sched.chunk = (a.sched.BH + 7) / 8;
+  const long long grid = sched_grid(a.sched);
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL>),
+                         dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      uint16_t* o, float* lse, hipStream_t stream) {
+  if (sh.D == 128) return sh.causal ? launch<128, true>(sh, q, k, v, o, lse, stream)
+                                    : launch<128, false>(sh, q, k, v, o, lse, stream);
+  return sh.causal ? launch<64, true>(sh, q, k, v, o, lse, stream)
+                   : launch<64, false>(sh, q, k, v, o, lse, stream);
+}
+
+}  // namespace tam
