@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--workload", default="llama2_70b_layer_s4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-groups", type=int, default=8)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, copy a MIB-mebibyte device buffer 3 times (a plain copy "
+                         "kernel of known size, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the attention path shards by independent (batch, kv-head) "
@@ -250,6 +253,15 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n * 4
+        del src, dst
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_groups)

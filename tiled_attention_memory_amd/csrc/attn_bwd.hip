@@ -127,24 +127,16 @@ struct DkdvArgs {
   TileSched sched;  // streams = (batch*Hkv + kv head) * nsplit + subset; tiles = key tiles
 };
 
-template <int D>
-struct DkdvLds {
-  static constexpr int STR = D + 8;
-  static constexpr int QT = kKBR * STR;       // Q tile
-  static constexpr int DOT = kKBR * STR;      // dO tile
-  static constexpr int STAGE = QT + DOT + 2 * kKBR * 2;  // + lse2, delta as fp32 (2 uint16 each)
-  static constexpr int ELEMS = 2 * STAGE;
-};
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(DkdvArgs a) {
-  using L = DkdvLds<D>;
+  using T = SwzTile<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int NCH = kKBR * CPR / kThreads;
-  static_assert(NCH * kThreads == kKBR * CPR, "tile must split evenly over the threads");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+  constexpr int NLD = T::LOADS / 4;             // 1-KiB loads per wave per tensor per tile
+  constexpr int STAGE = 2 * T::BYTES + 2 * kKBR * 4;  // Q tile, dO tile, lse2[64], delta[64]
+  static_assert(kKBR == T::ROWS, "query tile = LDS tile");
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
 
   int stream, t;
   if (!sched_decode(a.sched, blockIdx.x, &stream, &t)) return;
@@ -177,6 +169,20 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
     }
   }
 
+  // per-lane LDS offsets, fixed for every tile (see SwzTile)
+  const int i16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1);
+  int roff[KS], toff[DB][2], loff[NLD];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = T::chunk_off(col, 2 * ks + half);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+      toff[db][hi] = T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) loff[i] = T::load_src(wave * NLD + i, lane);
+
   const int NQ = (S + kKBR - 1) / kKBR;
   const int i_min = CAUSAL ? kvt0 / kKBR : 0;
   const int per_head = NQ - i_min;       // query tiles visited per head
@@ -187,44 +193,24 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
   auto step_head = [&](int st) { return h_first + st / per_head; };
   auto step_tile = [&](int st) { return NQ - 1 - st % per_head; };
 
-  u32x4 qreg[NCH], dreg[NCH];
-  float fl = 0.f;
-  auto gload = [&](int st) {
-    const int hq = step_head(st), it = step_tile(st);
-    const size_t qb = ((size_t)b * a.Hq + hq) * S * D;
+  // Q, dO tiles and their lse2, delta rows straight into an LDS stage; rows past S read as zeros.
+  auto issue = [&](int st, unsigned char* stage) {
+    const int hq = step_head(st), row0 = step_tile(st) * kKBR;
+    const size_t bh = (size_t)b * a.Hq + hq;
+    const int rows_left = S - row0;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + (bh * S + row0) * D, rows_left * D * 2);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + (bh * S + row0) * D, rows_left * D * 2);
+    unsigned char* dst = stage + wave * NLD * 1024;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int cidx = tid + kThreads * i;
-      const int r = cidx / CPR, cc = cidx % CPR;
-      const int row = it * kKBR + r;
-      if (row < S) {
-        const size_t off = qb + (size_t)row * D + cc * 8;
-        qreg[i] = *reinterpret_cast<const u32x4*>(a.q + off);
-        dreg[i] = *reinterpret_cast<const u32x4*>(a.dout + off);
-      } else {
-        qreg[i] = u32x4{0, 0, 0, 0};
-        dreg[i] = u32x4{0, 0, 0, 0};
-      }
+    for (int i = 0; i < NLD; ++i) {
+      load_lds16(rq, dst + i * 1024, loff[i]);
+      load_lds16(rd, dst + T::BYTES + i * 1024, loff[i]);
     }
-    if (tid < 2 * kKBR) {
-      const int r = tid & (kKBR - 1);
-      const int row = it * kKBR + r;
-      const size_t ro = ((size_t)b * a.Hq + hq) * S + row;
-      fl = row < S ? (tid < kKBR ? a.lse2[ro] : a.delta[ro]) : 0.f;
+    if (wave < 2) {
+      const float* src = wave == 0 ? a.lse2 : a.delta;
+      const __amdgpu_buffer_rsrc_t rf = make_rsrc(src + bh * S + row0, rows_left * 4);
+      load_lds4(rf, stage + 2 * T::BYTES + wave * kKBR * 4, lane * 4);
     }
-  };
-  auto lstore = [&](int stage) {
-    uint16_t* qs_ = smem + stage * L::STAGE;
-    uint16_t* ds_ = qs_ + L::QT;
-    float* fs_ = reinterpret_cast<float*>(ds_ + L::DOT);
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int cidx = tid + kThreads * i;
-      const int r = cidx / CPR, cc = cidx % CPR;
-      *reinterpret_cast<u32x4*>(qs_ + r * L::STR + cc * 8) = qreg[i];
-      *reinterpret_cast<u32x4*>(ds_ + r * L::STR + cc * 8) = dreg[i];
-    }
-    if (tid < 2 * kKBR) fs_[tid] = fl;  // [0, 64) lse2, [64, 128) delta
   };
 
   f32x16 acck[DB], accv[DB];
@@ -234,33 +220,24 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
     accv[db] = f32x16{};
   }
   const float c = a.c;
-  const int i16 = lane & 15;
-  const int dsub = 16 * ((lane >> 4) & 1);
 
-  if (nsteps > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int stage = st & 1;
-    if (st + 1 < nsteps) gload(st + 1);
+  auto step = [&](int st, const unsigned char* cur, unsigned char* nxt) {
+    if (st + 1 < nsteps) issue(st + 1, nxt);
     const int it = step_tile(st);
-    const uint16_t* Qs = smem + stage * L::STAGE;
-    const uint16_t* Ds = Qs + L::QT;
-    const float* Fs = reinterpret_cast<const float*>(Ds + L::DOT);
+    const unsigned char* Qs = cur;
+    const unsigned char* Ds = cur + T::BYTES;
+    const float* Fs = reinterpret_cast<const float*>(cur + 2 * T::BYTES);
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const int qb0 = it * kKBR + qs * 32;   // first query row of this sub-block
       if (CAUSAL && qb0 + 31 < kvb0) continue;  // every row is before every key of this wave
       // S[q][kv] and dP[q][kv]: lane holds key kvrow, rows qb0 + 8(v/4) + 4half + v%4
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const uint16_t* qp = Qs + (qs * 32 + col) * L::STR + 8 * half;
-      const uint16_t* dp_ = Ds + (qs * 32 + col) * L::STR + 8 * half;
+      f32x16 sc = f32x16{}, dp = f32x16{};
+      const int rb = qs * 32 * T::ROW_BYTES;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(lds_read_b128(qp + 16 * ks), kf[ks], s);
-        dp = mfma32(lds_read_b128(dp_ + 16 * ks), vf[ks], dp);
+        sc = mfma32(*reinterpret_cast<const bf16x8*>(Qs + rb + roff[ks]), kf[ks], sc);
+        dp = mfma32(*reinterpret_cast<const bf16x8*>(Ds + rb + roff[ks]), vf[ks], dp);
       }
       const bool masked = (CAUSAL && qb0 < kvb0 + 31) || qb0 + 32 > S || kvb0 + 32 > S;
       float p[16], ds[16];
@@ -272,7 +249,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * i + r;
-          float e = fast_exp2(fmaf(s[v], c, -l2[r]));
+          float e = fast_exp2(fmaf(sc[v], c, -l2[r]));
           if (masked) {
             const int qrow = it * kKBR + ql + r;
             const bool ok = qrow < S && kvrow < S && (!CAUSAL || kvrow <= qrow);
@@ -293,17 +270,27 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const int roff = (qs * 32 + k2 * 16 + 4 * half + (i16 >> 2)) * L::STR + db * 32 + dsub + 4 * (i16 & 3);
-          const bf16x8 a_do = lds_read_tr_pair(Ds + roff, Ds + roff + 8 * L::STR);
-          const bf16x8 a_q = lds_read_tr_pair(Qs + roff, Qs + roff + 8 * L::STR);
+          const int ro = (qs * 32 + k2 * 16) * T::ROW_BYTES;
+          const bf16x8 a_do = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(Ds + ro + toff[db][0]),
+                                               reinterpret_cast<const uint16_t*>(Ds + ro + toff[db][1]));
+          const bf16x8 a_q = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(Qs + ro + toff[db][0]),
+                                              reinterpret_cast<const uint16_t*>(Qs + ro + toff[db][1]));
           accv[db] = mfma32(a_do, ph[k2], accv[db]);
           accv[db] = mfma32(a_do, pl[k2], accv[db]);
           acck[db] = mfma32(a_q, dh[k2], acck[db]);
           acck[db] = mfma32(a_q, dl[k2], acck[db]);
         }
     }
-    if (st + 1 < nsteps) lstore(stage ^ 1);
+    wait_loads();
     __syncthreads();
+  };
+
+  if (nsteps > 0) issue(0, stage0);
+  wait_loads();
+  __syncthreads();
+  for (int st = 0; st < nsteps; st += 2) {
+    step(st, stage0, stage1);
+    if (st + 1 < nsteps) step(st + 1, stage1, stage0);
   }
 
   // lane holds key kvrow, head-dim entries 32db + 8i + 4half + (0..3)
@@ -378,25 +365,16 @@ struct DqArgs {
   TileSched sched;
 };
 
-template <int D>
-struct DqLds {
-  static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = D + 8;
-  static constexpr int KTILE = kQBC * KSTR;
-  static constexpr int VTILE = kQBC * VSTR;
-  static constexpr int STAGE = KTILE + VTILE;
-  static constexpr int ELEMS = 2 * STAGE;
-};
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dq_kernel(DqArgs a) {
-  using L = DqLds<D>;
+  using T = SwzTile<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int NCH = kQBC * CPR / kThreads;
-  static_assert(NCH * kThreads == kQBC * CPR, "tile must split evenly over the threads");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+  constexpr int NLD = T::LOADS / 4;
+  constexpr int STAGE = 2 * T::BYTES;   // K tile then V tile
+  static_assert(kQBC == T::ROWS, "key tile = LDS tile");
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
 
   int bh, qt;
   if (!sched_decode(a.sched, blockIdx.x, &bh, &qt)) return;
@@ -407,7 +385,8 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dq_kernel
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int kvh = h / (a.Hq / a.Hkv);
   const size_t q_base = (size_t)bh * S * D;
-  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
+  const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
+  const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
   const int q0 = qt * kQBR;
   const int wrow0 = q0 + wave * 32;
   const int qrow = wrow0 + col;
@@ -427,36 +406,34 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dq_kernel
   const float l2row = qrow < S ? a.lse2[(size_t)bh * S + qrow] : 0.f;
   const float drow = qrow < S ? a.delta[(size_t)bh * S + qrow] : 0.f;
 
+  // per-lane LDS offsets, fixed for every tile (see SwzTile)
+  const int i16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1);
+  int roff[KS], toff[DB][2], loff[NLD];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = T::chunk_off(col, 2 * ks + half);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+      toff[db][hi] = T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) loff[i] = T::load_src(wave * NLD + i, lane);
+
   const int last_row = min(q0 + kQBR, S) - 1;
   const int n_kv = (S + kQBC - 1) / kQBC;
   const int ntiles = CAUSAL ? min(n_kv, last_row / kQBC + 1) : n_kv;
 
-  u32x4 kreg[NCH], vreg[NCH];
-  auto gload = [&](int j) {
+  auto issue = [&](int j, unsigned char* stage) {
+    const int row0 = j * kQBC;
+    const int bytes = (S - row0) * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)row0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)row0 * D, bytes);
+    unsigned char* dst = stage + wave * NLD * 1024;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int cidx = tid + kThreads * i;
-      const int r = cidx / CPR, cc = cidx % CPR;
-      const int row = j * kQBC + r;
-      if (row < S) {
-        const size_t off = kv_base + (size_t)row * D + cc * 8;
-        kreg[i] = *reinterpret_cast<const u32x4*>(a.k + off);
-        vreg[i] = *reinterpret_cast<const u32x4*>(a.v + off);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int stage) {
-    uint16_t* ks_ = smem + stage * L::STAGE;
-    uint16_t* vs_ = ks_ + L::KTILE;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int cidx = tid + kThreads * i;
-      const int r = cidx / CPR, cc = cidx % CPR;
-      *reinterpret_cast<u32x4*>(ks_ + r * L::KSTR + cc * 8) = kreg[i];
-      *reinterpret_cast<u32x4*>(vs_ + r * L::VSTR + cc * 8) = vreg[i];
+    for (int i = 0; i < NLD; ++i) {
+      load_lds16(rk, dst + i * 1024, loff[i]);
+      load_lds16(rv, dst + T::BYTES + i * 1024, loff[i]);
     }
   };
 
@@ -468,74 +445,69 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dq_kernel
   }
   float csum = 0.f;  // this lane's half of c = sum_j dS~_j for its row
   const float c = a.c;
-  const int i16 = lane & 15;
-  const int dsub = 16 * ((lane >> 4) & 1);
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int stage = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
+  auto step = [&](int j, const unsigned char* cur, unsigned char* nxt) {
+    if (j + 1 < ntiles) issue(j + 1, nxt);
     const int kv0 = j * kQBC;
     const bool active = !CAUSAL || kv0 <= wrow0 + 31;
     if (active) {
-      const uint16_t* Ks = smem + stage * L::STAGE;
-      const uint16_t* Vs = Ks + L::KTILE;
-      f32x16 s[2], dp[2];
+      const unsigned char* Ks = cur;
+      const unsigned char* Vs = cur + T::BYTES;
+      const bool masked = (kv0 + kQBC > S) || (CAUSAL && kv0 + kQBC - 1 > wrow0);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
-        const uint16_t* kp = Ks + (kb * 32 + col) * L::KSTR + 8 * half;
-        const uint16_t* vp = Vs + (kb * 32 + col) * L::VSTR + 8 * half;
+        // S^T and dP^T for 32 keys: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow
+        f32x16 sc = f32x16{}, dp = f32x16{};
+        const int rb = kb * 32 * T::ROW_BYTES;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s[kb] = mfma32(lds_read_b128(kp + 16 * ks), qf[ks], s[kb]);
-          dp[kb] = mfma32(lds_read_b128(vp + 16 * ks), df[ks], dp[kb]);
+          sc = mfma32(*reinterpret_cast<const bf16x8*>(Ks + rb + roff[ks]), qf[ks], sc);
+          dp = mfma32(*reinterpret_cast<const bf16x8*>(Vs + rb + roff[ks]), df[ks], dp);
         }
-      }
-      const bool masked = (kv0 + kQBC > S) || (CAUSAL && kv0 + kQBC - 1 > wrow0);
-      bf16x8 dh[2][2], dl[2][2], ph[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
         float ds[16], pf[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float e = fast_exp2(fmaf(s[kb][v], c, -l2row));
+          float e = fast_exp2(fmaf(sc[v], c, -l2row));
           if (masked) {
             const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
             const bool ok = kv < S && (!CAUSAL || kv <= qrow);
             e = ok ? e : 0.f;
           }
           pf[v] = e;
-          ds[v] = e * (dp[kb][v] - drow);
+          ds[v] = e * (dp[v] - drow);
           csum += ds[v];
         }
+        bf16x8 dh[2], dl[2], ph[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          split_bf16x8(ds + 8 * k2, &dh[kb][k2], &dl[kb][k2]);
-          ph[kb][k2] = pack_bf16x8(pf + 8 * k2);
+          split_bf16x8(ds + 8 * k2, &dh[k2], &dl[k2]);
+          ph[k2] = pack_bf16x8(pf + 8 * k2);
         }
-      }
-      // dQ^T += K^T dS~^T (hi and lo parts) and (PK)^T += K^T P^T: K read transposed
-      // from its row-major tile once for all three products.
+        // dQ^T += K^T dS~^T (hi and lo parts) and (PK)^T += K^T P^T: K read transposed
+        // from its row-major tile once for all three products.
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int k2 = 0; k2 < 2; ++k2) {
-            const uint16_t* kp =
-                Ks + (kb * 32 + k2 * 16 + 4 * half + (i16 >> 2)) * L::KSTR + db * 32 + dsub + 4 * (i16 & 3);
-            const bf16x8 a_k = lds_read_tr_pair(kp, kp + 8 * L::KSTR);
-            acc[db] = mfma32(a_k, dh[kb][k2], acc[db]);
-            acc[db] = mfma32(a_k, dl[kb][k2], acc[db]);
-            accpk[db] = mfma32(a_k, ph[kb][k2], accpk[db]);
+            const int ro = (kb * 32 + k2 * 16) * T::ROW_BYTES;
+            const bf16x8 a_k = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][0]),
+                                                reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][1]));
+            acc[db] = mfma32(a_k, dh[k2], acc[db]);
+            acc[db] = mfma32(a_k, dl[k2], acc[db]);
+            accpk[db] = mfma32(a_k, ph[k2], accpk[db]);
           }
+      }
     }
-    if (j + 1 < ntiles) lstore(stage ^ 1);
+    wait_loads();
     __syncthreads();
+  };
+
+  issue(0, stage0);
+  wait_loads();
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, stage0, stage1);
+    if (j + 1 < ntiles) step(j + 1, stage1, stage0);
   }
 
   const float corr = sum_halves(csum);  // Delta_i - Delta~_i
@@ -545,10 +517,10 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dq_kernel
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float g[4];
+        float gq[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) g[r] = a.scale * fmaf(-corr, accpk[db][4 * i + r], acc[db][4 * i + r]);
-        u32x2 w = {pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3])};
+        for (int r = 0; r < 4; ++r) gq[r] = a.scale * fmaf(-corr, accpk[db][4 * i + r], acc[db][4 * i + r]);
+        u32x2 w = {pack_bf16(gq[0], gq[1]), pack_bf16(gq[2], gq[3])};
         *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i) = w;
       }
     if (half == 0) a.delta[(size_t)bh * S + qrow] = drow + corr;

@@ -111,6 +111,77 @@ __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8* hi, bf16x8*
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
 
+// ---------------------------------------------------------------------------
+// 64-row LDS tiles of bf16 rows, filled straight from global memory
+// ---------------------------------------------------------------------------
+// Layout: 256-byte lines (one row of D = 128, or two rows of D = 64) whose
+// 16-byte chunks are XOR-swizzled by the line index. The swizzle is chosen so
+// that both read patterns the kernels use touch every LDS bank exactly once
+// per cycle (checked with the LDS bank-conflict counter on the device):
+//   * row reads: 16 lanes read the same 16-byte chunk of 16 consecutive rows;
+//   * transposed 4x16 reads: 32 lanes read four 64-byte row segments of four
+//     consecutive rows.
+// For D = 128, chunk c of row r sits at chunk c ^ f(r) of line r with
+// f(r) = ((r & 3) << 2) | ((r >> 2) & 3): a permutation of the 16 chunks over
+// any 16 rows, giving the four rows of each aligned group distinct 64-byte
+// groups. For D = 64, row r is half (r & 1) of line r / 2 and the 16 chunk
+// slots are XORed with g(L) = ((L & 1) << 2) | ((L >> 1) & 3).
+// The swizzle repeats every 16 rows, so moving by a multiple of 16 rows moves
+// every address by the same number of bytes.
+template <int D>
+struct SwzTile {
+  static_assert(D == 64 || D == 128, "head dim");
+  static constexpr int ROWS = 64;
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int BYTES = ROWS * ROW_BYTES;   // 16 KiB or 8 KiB
+  static constexpr int LOADS = BYTES / 1024;       // wave-wide 16-byte-per-lane loads per tile
+
+  // byte offset of the 16-byte chunk c (elements 8c..8c+7) of row r
+  __host__ __device__ static constexpr int chunk_off(int r, int c) {
+    return D == 128 ? r * 256 + ((c ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 4)
+                    : (r >> 1) * 256 +
+                          (((((r & 1) << 3) | c) ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))) << 4);
+  }
+  // byte offset of element e (a multiple of 4) of row r
+  __host__ __device__ static constexpr int elem_off(int r, int e) {
+    return chunk_off(r, e >> 3) + ((e & 7) << 1);
+  }
+  // Source of the 16 bytes that lane l of the i-th 1-KiB load writes (LDS bytes
+  // 1024 i + 16 l): byte offset of that chunk within the tile's rows in global memory.
+  __host__ __device__ static constexpr int load_src(int i, int l) {
+    return D == 128 ? src128(4 * i + (l >> 4), l & 15) : src64(4 * i + (l >> 4), l & 15);
+  }
+
+ private:
+  __host__ __device__ static constexpr int src128(int line, int slot) {
+    return line * 256 + ((slot ^ (((line & 3) << 2) | ((line >> 2) & 3))) << 4);
+  }
+  __host__ __device__ static constexpr int src64(int line, int slot) {
+    return (2 * line + ((slot ^ (((line & 1) << 2) | ((line >> 1) & 3))) >> 3)) * 128 +
+           (((slot ^ (((line & 1) << 2) | ((line >> 1) & 3))) & 7) << 4);
+  }
+};
+
+// Buffer descriptor over `bytes` bytes from `base`: loads past the end read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// 16 bytes per lane from rsrc + voffset into LDS at lds_base + 16 * lane
+// (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           voffset, 0, 0, 0);
+}
+// 4 bytes per lane into LDS at lds_base + 4 * lane.
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, void* lds_base, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4,
+                                           voffset, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding global loads (including loads into LDS) are done.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Scheduler shared by the query-tile kernels: work unit = (query head, query
 // tile). Workgroup i runs on XCD i % 8; XCD x owns a contiguous range of
 // heads (so the heads of one key/value group share that XCD's L2) and walks

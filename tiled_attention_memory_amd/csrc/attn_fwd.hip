@@ -14,8 +14,8 @@
 //                      per-lane scalars; one cross-half exchange per tile)
 //   O^T += V^T P^T    (MFMA; A = V read transposed from LDS, B = P straight
 //                      from the S^T accumulator after bf16 rounding)
-// K/V tiles are staged through double-buffered LDS by all 256 threads with
-// coalesced 16-byte loads; the next tile's loads are in flight while the
+// K/V tiles go from global memory straight into double-buffered, swizzled LDS
+// (no staging registers); the next tile's loads are in flight while the
 // current one is consumed. Under a causal mask, key tiles past the diagonal
 // are never visited and only tiles that straddle it evaluate the mask.
 #include <math.h>
@@ -41,25 +41,24 @@ struct FwdArgs {
   TileSched sched;
 };
 
-template <int D>
-struct FwdLds {
-  static constexpr int KSTR = D + 8;    // K rows: 16-byte reads along a row, conflict-free with +16 B pad
-  static constexpr int VSTR = D + 16;   // V rows: transposed 4x16 block reads, +32 B pad
-  static constexpr int KTILE = kBC * KSTR;
-  static constexpr int VTILE = kBC * VSTR;
-  static constexpr int STAGE = KTILE + VTILE;
-  static constexpr int ELEMS = 2 * STAGE;
-};
+// The running row max only moves when a tile's max exceeds it by more than
+// this (base-2 units); probabilities then stay below 2^8 before normalisation,
+// which fp32 sums and bf16 products carry without loss, and the O rescale is
+// skipped for most tiles.
+constexpr float kLazyMax = 8.f;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
-  using L = FwdLds<D>;
-  constexpr int KS = D / 16;                  // MFMA k-steps over the head dimension
-  constexpr int DB = D / 32;                  // 32-row blocks of the O^T accumulator
-  constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
-  constexpr int NCH = kBC * CPR / kThreads;   // chunks per thread per tensor per tile
-  static_assert(NCH * kThreads == kBC * CPR, "tile must split evenly over the threads");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+  using T = SwzTile<D>;
+  constexpr int KS = D / 16;          // MFMA k-steps over the head dimension
+  constexpr int DB = D / 32;          // 32-row blocks of the O^T accumulator
+  constexpr int STAGE = 2 * T::BYTES; // K tile then V tile
+  constexpr int NLD = T::LOADS / 4;   // 1-KiB loads per wave per tensor per tile
+  static_assert(kBC == T::ROWS, "key tile = LDS tile");
+  // Two separate LDS stages, so that loads into one are provably independent
+  // of reads from the other and need no wait before those reads.
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
 
   int bh, qt;
   if (!sched_decode(a.sched, blockIdx.x, &bh, &qt)) return;
@@ -70,7 +69,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int kvh = h / (a.Hq / a.Hkv);
   const size_t q_base = (size_t)bh * S * D;
-  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
+  const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
+  const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
   const int q0 = qt * kBR;
   const int wrow0 = q0 + wave * 32;  // first query row of this wave
   const int qrow = wrow0 + col;      // the query row this lane owns
@@ -85,73 +85,71 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
                         : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
 
+  // Per-lane LDS offsets, fixed for every tile: row reads of K (row col, chunk
+  // 2ks + half; key block kb adds 32 rows) and transposed reads of V (rows
+  // 4half + (lane&15)/4 and +8, elements 32db + dsub + 4(lane&3); blocks of 16
+  // keys add 16 rows).
+  const int i16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1);
+  int koff[KS], voff[DB][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = T::chunk_off(col, 2 * ks + half);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+      voff[db][hi] = T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
+  int loff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) loff[i] = T::load_src(wave * NLD + i, lane);
+
   const int last_row = min(q0 + kBR, S) - 1;
   const int n_kv = (S + kBC - 1) / kBC;
   const int ntiles = CAUSAL ? min(n_kv, last_row / kBC + 1) : n_kv;
 
-  u32x4 kreg[NCH], vreg[NCH];
-  auto gload = [&](int j) {
+  // K and V tile j straight into an LDS stage; rows past S read as zeros.
+  auto issue = [&](int j, unsigned char* stage) {
+    const int row0 = j * kBC;
+    const int bytes = (S - row0) * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)row0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)row0 * D, bytes);
+    unsigned char* dst = stage + wave * NLD * 1024;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int cidx = tid + kThreads * i;
-      const int r = cidx / CPR, cc = cidx % CPR;
-      const int row = j * kBC + r;
-      if (row < S) {
-        const size_t off = kv_base + (size_t)row * D + cc * 8;
-        kreg[i] = *reinterpret_cast<const u32x4*>(a.k + off);
-        vreg[i] = *reinterpret_cast<const u32x4*>(a.v + off);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int stage) {
-    uint16_t* ks_ = smem + stage * L::STAGE;
-    uint16_t* vs_ = ks_ + L::KTILE;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int cidx = tid + kThreads * i;
-      const int r = cidx / CPR, cc = cidx % CPR;
-      *reinterpret_cast<u32x4*>(ks_ + r * L::KSTR + cc * 8) = kreg[i];
-      *reinterpret_cast<u32x4*>(vs_ + r * L::VSTR + cc * 8) = vreg[i];
+    for (int i = 0; i < NLD; ++i) {
+      load_lds16(rk, dst + i * 1024, loff[i]);
+      load_lds16(rv, dst + T::BYTES + i * 1024, loff[i]);
     }
   };
 
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float m_run = -INFINITY;  // running max of this row's base-2 scaled scores
+  float m_run = -INFINITY;  // running (lazy) max of this row's base-2 scaled scores
   float l_run = 0.f;        // running sum of this lane's half of the row
   const float c = a.c;
   const bool c_nonneg = c >= 0.f;
   const float fill = c_nonneg ? -INFINITY : INFINITY;  // masked score: never the extreme
 
-  // transposed-read coordinates of this lane inside its 16-lane group
-  const int i16 = lane & 15;
-  const int dsub = 16 * ((lane >> 4) & 1);
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int stage = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
+  auto step = [&](int j, const unsigned char* cur, unsigned char* nxt) {
+    if (j + 1 < ntiles) issue(j + 1, nxt);
     const int kv0 = j * kBC;
     const bool active = !CAUSAL || kv0 <= wrow0 + 31;
     if (active) {
-      const uint16_t* Ks = smem + stage * L::STAGE;
-      const uint16_t* Vs = Ks + L::KTILE;
+      const unsigned char* Ks = cur;
+      const unsigned char* Vs = cur + T::BYTES;
 
       // S^T for two 32-key blocks: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow.
-      f32x16 s[2];
+      bf16x8 kop[2][KS];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const uint16_t* kp = Ks + (kb * 32 + col) * L::KSTR + 8 * half;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s[kb] = mfma32(lds_read_b128(kp + 16 * ks), qf[ks], s[kb]);
-      }
+        for (int ks = 0; ks < KS; ++ks)
+          kop[kb][ks] = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * T::ROW_BYTES + koff[ks]);
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kop[kb][ks], qf[ks], s[kb]);
 
       const bool masked = (kv0 + kBC > S) || (CAUSAL && kv0 + kBC - 1 > wrow0);
       if (masked) {
@@ -181,10 +179,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         ext = min_halves(ext);
       }
       // A tile where all of this row's keys are masked gives NaN (c == 0) or -inf
-      // here; fmaxf keeps the running max in both cases.
-      const float m_new = fmaxf(m_run, ext * c);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
+      // here; neither moves the running max.
+      const float mt = ext * c;
+      const bool grow = mt > m_run + kLazyMax;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mt : m_run;
+        const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, 1 where unchanged
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      }
 
       float p[2][16];
       float lsum = 0.f;
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float e = fast_exp2(fmaf(s[kb][v], c, -m_new));
+          float e = fast_exp2(fmaf(s[kb][v], c, -m_run));
           if (masked) {
             const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
             const bool ok = kv < S && (!CAUSAL || kv <= qrow);
@@ -201,9 +206,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
           p[kb][v] = e;
           lsum += e;
         }
-      l_run = fmaf(l_run, alpha, lsum);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      l_run += lsum;
 
       bf16x8 pb[2][2];
 #pragma unroll
@@ -214,18 +217,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       // O^T += V^T P^T: the k index of MFMA (kb, k2) slot t of lane half hh is key
       // 32kb + 16k2 + 8(t/4) + 4hh + t%4, matching where P sits in the S^T accumulator.
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db) {
+        bf16x8 vop[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int k2 = 0; k2 < 2; ++k2) {
-            const uint16_t* vp =
-                Vs + (kb * 32 + k2 * 16 + 4 * half + (i16 >> 2)) * L::VSTR + db * 32 + dsub + 4 * (i16 & 3);
-            acc[db] = mfma32(lds_read_tr_pair(vp, vp + 8 * L::VSTR), pb[kb][k2], acc[db]);
+            const unsigned char* vp = Vs + (kb * 32 + k2 * 16) * T::ROW_BYTES;
+            vop[kb][k2] = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(vp + voff[db][0]),
+                                           reinterpret_cast<const uint16_t*>(vp + voff[db][1]));
           }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) acc[db] = mfma32(vop[kb][k2], pb[kb][k2], acc[db]);
+      }
     }
-    if (j + 1 < ntiles) lstore(stage ^ 1);
+    wait_loads();
     __syncthreads();
+  };
+
+  issue(0, stage0);
+  wait_loads();
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, stage0, stage1);
+    if (j + 1 < ntiles) step(j + 1, stage1, stage0);
   }
 
   const float l_tot = sum_halves(l_run);
