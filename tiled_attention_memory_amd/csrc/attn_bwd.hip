@@ -32,6 +32,8 @@
 // results are bitwise reproducible.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -128,7 +130,7 @@ struct DkdvArgs {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(DkdvArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(DkdvArgs a) {
   using T = SwzTile<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -147,7 +149,8 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
   const int hps = g / a.nsplit;           // query heads per subset
   const int h_first = kvh * g + sub * hps;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
   const int col = lane & 31, half = lane >> 5;
   const int S = a.S;
   const size_t kv_base = (size_t)grp * S * D;
@@ -221,51 +224,66 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
   }
   const float c = a.c;
 
-  auto step = [&](int st, const unsigned char* cur, unsigned char* nxt) {
-    if (st + 1 < nsteps) issue(st + 1, nxt);
-    const int it = step_tile(st);
+  // One 64-row query tile against this wave's 32 keys, as two 32-row blocks.
+  // The products of both blocks are issued before either block's elementwise
+  // work, so one block's VALU work can run under the other's MFMAs. MASKED:
+  // the tile meets the diagonal or the end of the sequence; hidden (query, key)
+  // pairs get P = 0 and blocks entirely before this wave's keys are skipped.
+  auto tile = [&](auto masked_tag, int it, const unsigned char* cur) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const unsigned char* Qs = cur;
     const unsigned char* Ds = cur + T::BYTES;
     const float* Fs = reinterpret_cast<const float*>(cur + 2 * T::BYTES);
+    bool run[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) run[qs] = !(MASKED && CAUSAL && it * kKBR + qs * 32 + 31 < kvb0);
+
+    // S[q][kv] and dP[q][kv]: lane holds key kvrow, rows it*64 + 32qs + 8(v/4) + 4half + v%4
+    f32x16 sc[2], dp[2];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-      const int qb0 = it * kKBR + qs * 32;   // first query row of this sub-block
-      if (CAUSAL && qb0 + 31 < kvb0) continue;  // every row is before every key of this wave
-      // S[q][kv] and dP[q][kv]: lane holds key kvrow, rows qb0 + 8(v/4) + 4half + v%4
-      f32x16 sc = f32x16{}, dp = f32x16{};
+      sc[qs] = f32x16{};
+      dp[qs] = f32x16{};
+      if (!run[qs]) continue;
       const int rb = qs * 32 * T::ROW_BYTES;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        sc = mfma32(*reinterpret_cast<const bf16x8*>(Qs + rb + roff[ks]), kf[ks], sc);
-        dp = mfma32(*reinterpret_cast<const bf16x8*>(Ds + rb + roff[ks]), vf[ks], dp);
+        sc[qs] = mfma32(*reinterpret_cast<const bf16x8*>(Qs + rb + roff[ks]), kf[ks], sc[qs]);
+        dp[qs] = mfma32(*reinterpret_cast<const bf16x8*>(Ds + rb + roff[ks]), vf[ks], dp[qs]);
       }
-      const bool masked = (CAUSAL && qb0 < kvb0 + 31) || qb0 + 32 > S || kvb0 + 32 > S;
+    }
+    bf16x8 ph[2][2], pl[2][2], dh[2][2], dl[2][2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
       float p[16], ds[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ql = qs * 32 + 8 * i + 4 * half;   // local row of v = 4i
         const f32x4 l2 = *reinterpret_cast<const f32x4*>(Fs + ql);
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(Fs + kKBR + ql);
+        const f32x4 dlt = *reinterpret_cast<const f32x4*>(Fs + kKBR + ql);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * i + r;
-          float e = fast_exp2(fmaf(sc[v], c, -l2[r]));
-          if (masked) {
+          float e = fast_exp2(fmaf(sc[qs][v], c, -l2[r]));
+          if (MASKED) {
             const int qrow = it * kKBR + ql + r;
             const bool ok = qrow < S && kvrow < S && (!CAUSAL || kvrow <= qrow);
             e = ok ? e : 0.f;
           }
           p[v] = e;
-          ds[v] = e * (dp[v] - dl[r]);
+          ds[v] = e * (dp[qs][v] - dlt[r]);
         }
       }
-      bf16x8 ph[2], pl[2], dh[2], dl[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        split_bf16x8(p + 8 * k2, &ph[k2], &pl[k2]);
-        split_bf16x8(ds + 8 * k2, &dh[k2], &dl[k2]);
+        split_bf16x8(p + 8 * k2, &ph[qs][k2], &pl[qs][k2]);
+        split_bf16x8(ds + 8 * k2, &dh[qs][k2], &dl[qs][k2]);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS; A operands read transposed from the row-major tiles.
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS; A operands read transposed from the row-major tiles.
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      if (!run[qs]) continue;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -275,12 +293,24 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkdv_kern
                                                reinterpret_cast<const uint16_t*>(Ds + ro + toff[db][1]));
           const bf16x8 a_q = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(Qs + ro + toff[db][0]),
                                               reinterpret_cast<const uint16_t*>(Qs + ro + toff[db][1]));
-          accv[db] = mfma32(a_do, ph[k2], accv[db]);
-          accv[db] = mfma32(a_do, pl[k2], accv[db]);
-          acck[db] = mfma32(a_q, dh[k2], acck[db]);
-          acck[db] = mfma32(a_q, dl[k2], acck[db]);
+          accv[db] = mfma32(a_do, ph[qs][k2], accv[db]);
+          accv[db] = mfma32(a_do, pl[qs][k2], accv[db]);
+          acck[db] = mfma32(a_q, dh[qs][k2], acck[db]);
+          acck[db] = mfma32(a_q, dl[qs][k2], acck[db]);
         }
     }
+  };
+
+  auto step = [&](int st, const unsigned char* cur, unsigned char* nxt) {
+    if (st + 1 < nsteps) issue(st + 1, nxt);
+    const int it = step_tile(st);
+    // the whole workgroup takes the same branch: the tile meets the diagonal of
+    // the unit's 128 keys, or the end of the sequence
+    const bool masked = (CAUSAL && it * kKBR < kvt0 + kKBC) || it * kKBR + kKBR > S || kvt0 + kKBC > S;
+    if (masked)
+      tile(std::true_type{}, it, cur);
+    else
+      tile(std::false_type{}, it, cur);
     wait_loads();
     __syncthreads();
   };
@@ -366,7 +396,7 @@ struct DqArgs {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dq_kernel(DqArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(DqArgs a) {
   using T = SwzTile<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -379,7 +409,8 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dq_kernel
   int bh, qt;
   if (!sched_decode(a.sched, blockIdx.x, &bh, &qt)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
   const int col = lane & 31, half = lane >> 5;
   const int S = a.S;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
@@ -446,57 +477,75 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dq_kernel
   float csum = 0.f;  // this lane's half of c = sum_j dS~_j for its row
   const float c = a.c;
 
+  // One 64-key tile as two 32-key blocks; the products of both blocks are
+  // issued before either block's elementwise work. MASKED: the tile meets this
+  // wave's diagonal or the end of the sequence.
+  auto tile = [&](auto masked_tag, int kv0, const unsigned char* cur) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const unsigned char* Ks = cur;
+    const unsigned char* Vs = cur + T::BYTES;
+    // S^T and dP^T for 32 keys: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow
+    f32x16 sc[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = f32x16{};
+      dp[kb] = f32x16{};
+      const int rb = kb * 32 * T::ROW_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + rb + roff[ks]), qf[ks], sc[kb]);
+        dp[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Vs + rb + roff[ks]), df[ks], dp[kb]);
+      }
+    }
+    bf16x8 dh[2][2], dl[2][2], ph[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float ds[16], pf[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float e = fast_exp2(fmaf(sc[kb][v], c, -l2row));
+        if (MASKED) {
+          const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          const bool ok = kv < S && (!CAUSAL || kv <= qrow);
+          e = ok ? e : 0.f;
+        }
+        pf[v] = e;
+        ds[v] = e * (dp[kb][v] - drow);
+        csum += ds[v];
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        split_bf16x8(ds + 8 * k2, &dh[kb][k2], &dl[kb][k2]);
+        ph[kb][k2] = pack_bf16x8(pf + 8 * k2);
+      }
+    }
+    // dQ^T += K^T dS~^T (hi and lo parts) and (PK)^T += K^T P^T: K read transposed
+    // from its row-major tile once for all three products.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int ro = (kb * 32 + k2 * 16) * T::ROW_BYTES;
+          const bf16x8 a_k = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][0]),
+                                              reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][1]));
+          acc[db] = mfma32(a_k, dh[kb][k2], acc[db]);
+          acc[db] = mfma32(a_k, dl[kb][k2], acc[db]);
+          accpk[db] = mfma32(a_k, ph[kb][k2], accpk[db]);
+        }
+  };
+
   auto step = [&](int j, const unsigned char* cur, unsigned char* nxt) {
     if (j + 1 < ntiles) issue(j + 1, nxt);
     const int kv0 = j * kQBC;
     const bool active = !CAUSAL || kv0 <= wrow0 + 31;
     if (active) {
-      const unsigned char* Ks = cur;
-      const unsigned char* Vs = cur + T::BYTES;
       const bool masked = (kv0 + kQBC > S) || (CAUSAL && kv0 + kQBC - 1 > wrow0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // S^T and dP^T for 32 keys: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow
-        f32x16 sc = f32x16{}, dp = f32x16{};
-        const int rb = kb * 32 * T::ROW_BYTES;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          sc = mfma32(*reinterpret_cast<const bf16x8*>(Ks + rb + roff[ks]), qf[ks], sc);
-          dp = mfma32(*reinterpret_cast<const bf16x8*>(Vs + rb + roff[ks]), df[ks], dp);
-        }
-        float ds[16], pf[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float e = fast_exp2(fmaf(sc[v], c, -l2row));
-          if (masked) {
-            const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-            const bool ok = kv < S && (!CAUSAL || kv <= qrow);
-            e = ok ? e : 0.f;
-          }
-          pf[v] = e;
-          ds[v] = e * (dp[v] - drow);
-          csum += ds[v];
-        }
-        bf16x8 dh[2], dl[2], ph[2];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          split_bf16x8(ds + 8 * k2, &dh[k2], &dl[k2]);
-          ph[k2] = pack_bf16x8(pf + 8 * k2);
-        }
-        // dQ^T += K^T dS~^T (hi and lo parts) and (PK)^T += K^T P^T: K read transposed
-        // from its row-major tile once for all three products.
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const int ro = (kb * 32 + k2 * 16) * T::ROW_BYTES;
-            const bf16x8 a_k = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][0]),
-                                                reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][1]));
-            acc[db] = mfma32(a_k, dh[k2], acc[db]);
-            acc[db] = mfma32(a_k, dl[k2], acc[db]);
-            accpk[db] = mfma32(a_k, ph[k2], accpk[db]);
-          }
-      }
+      if (masked)
+        tile(std::true_type{}, kv0, cur);
+      else
+        tile(std::false_type{}, kv0, cur);
     }
     wait_loads();
     __syncthreads();

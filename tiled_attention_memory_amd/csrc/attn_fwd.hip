@@ -20,6 +20,8 @@
 // are never visited and only tiles that straddle it evaluate the mask.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -63,7 +65,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   int bh, qt;
   if (!sched_decode(a.sched, blockIdx.x, &bh, &qt)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
   const int col = lane & 31, half = lane >> 5;
   const int S = a.S;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
@@ -75,14 +78,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int wrow0 = q0 + wave * 32;  // first query row of this wave
   const int qrow = wrow0 + col;      // the query row this lane owns
 
-  // Q rows as MFMA B operands (k = head dim), resident for the whole loop.
+  // Q rows as MFMA B operands (k = head dim), resident for the whole loop. A
+  // negative scale is folded into Q (an exact sign flip), so the softmax below
+  // always works with a scale c >= 0 and takes a row max.
+  const float c = fabsf(a.c);
   bf16x8 qf[KS];
   {
     const uint16_t* qp = a.q + q_base + (size_t)qrow * D + 8 * half;
+    const uint32_t flip = a.c < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = qrow < S ? *reinterpret_cast<const bf16x8*>(qp + 16 * ks)
-                        : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w = qrow < S ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      w ^= flip;
+      qf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
   }
 
   // Per-lane LDS offsets, fixed for every tile: row reads of K (row col, chunk
@@ -126,123 +135,133 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY;  // running (lazy) max of this row's base-2 scaled scores
   float l_run = 0.f;        // running sum of this lane's half of the row
-  const float c = a.c;
-  const bool c_nonneg = c >= 0.f;
-  const float fill = c_nonneg ? -INFINITY : INFINITY;  // masked score: never the extreme
 
-  auto step = [&](int j, const unsigned char* cur, unsigned char* nxt) {
-    if (j + 1 < ntiles) issue(j + 1, nxt);
-    const int kv0 = j * kBC;
-    const bool active = !CAUSAL || kv0 <= wrow0 + 31;
-    if (active) {
-      const unsigned char* Ks = cur;
-      const unsigned char* Vs = cur + T::BYTES;
+  // One 64-key tile. MASKED: the tile straddles the diagonal or the end of the
+  // sequence for this wave, so scores of hidden keys are excluded; every other
+  // tile runs without any per-element test.
+  auto tile = [&](auto masked_tag, int kv0, const unsigned char* cur) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const unsigned char* Ks = cur;
+    const unsigned char* Vs = cur + T::BYTES;
 
-      // S^T for two 32-key blocks: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow.
-      bf16x8 kop[2][KS];
+    // S^T for two 32-key blocks: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow.
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kop[kb][ks] = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * T::ROW_BYTES + koff[ks]);
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 kop[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
+        kop[ks] = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * T::ROW_BYTES + koff[ks]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kop[kb][ks], qf[ks], s[kb]);
-
-      const bool masked = (kv0 + kBC > S) || (CAUSAL && kv0 + kBC - 1 > wrow0);
-      if (masked) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-            const bool ok = kv < S && (!CAUSAL || kv <= qrow);
-            if (!ok) s[kb][v] = fill;
-          }
-      }
-
-      // row extreme of the raw scores (max if the scale is >= 0, else min)
-      float ext = s[0][0];
-      if (c_nonneg) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) ext = fmaxf(ext, s[kb][v]);
-        ext = max_halves(ext);
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) ext = fminf(ext, s[kb][v]);
-        ext = min_halves(ext);
-      }
-      // A tile where all of this row's keys are masked gives NaN (c == 0) or -inf
-      // here; neither moves the running max.
-      const float mt = ext * c;
-      const bool grow = mt > m_run + kLazyMax;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mt : m_run;
-        const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, 1 where unchanged
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-      }
-
-      float p[2][16];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float e = fast_exp2(fmaf(s[kb][v], c, -m_run));
-          if (masked) {
-            const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-            const bool ok = kv < S && (!CAUSAL || kv <= qrow);
-            e = ok ? e : 0.f;
-          }
-          p[kb][v] = e;
-          lsum += e;
-        }
-      l_run += lsum;
-
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) pb[kb][k2] = pack_bf16x8(&p[kb][8 * k2]);
-
-      // O^T += V^T P^T: the k index of MFMA (kb, k2) slot t of lane half hh is key
-      // 32kb + 16k2 + 8(t/4) + 4hh + t%4, matching where P sits in the S^T accumulator.
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        bf16x8 vop[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const unsigned char* vp = Vs + (kb * 32 + k2 * 16) * T::ROW_BYTES;
-            vop[kb][k2] = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(vp + voff[db][0]),
-                                           reinterpret_cast<const uint16_t*>(vp + voff[db][1]));
-          }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) acc[db] = mfma32(vop[kb][k2], pb[kb][k2], acc[db]);
-      }
+      for (int ks = 0; ks < KS; ++ks) s[kb] = mfma32(kop[ks], qf[ks], s[kb]);
     }
+
+    // key of accumulator element v of block kb, and whether this row may see it
+    auto visible = [&](int kb, int v) {
+      const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      return kv < S && (!CAUSAL || kv <= qrow);
+    };
+    if (MASKED) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb][v] = visible(kb, v) ? s[kb][v] : -INFINITY;
+    }
+    float ext = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ext = fmaxf(ext, s[kb][v]);
+    ext = max_halves(ext);
+    // A tile where all of this row's keys are masked gives -inf, or NaN when
+    // c == 0; neither moves the running max.
+    const float mt = ext * c;
+    const bool grow = mt > m_run + kLazyMax;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, 1 where unchanged
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+
+    float p[2][16];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float e = fast_exp2(fmaf(s[kb][v], c, -m_run));
+        if (MASKED) e = visible(kb, v) ? e : 0.f;  // also covers c == 0, where -inf * c is NaN
+        p[kb][v] = e;
+        lsum += e;
+      }
+    l_run += lsum;
+
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) pb[kb][k2] = pack_bf16x8(&p[kb][8 * k2]);
+
+    // Keep the V reads below this point: hoisting them over the softmax would
+    // hold 64 more registers and cost the second wave per SIMD.
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T += V^T P^T: the k index of MFMA (kb, k2) slot t of lane half hh is key
+    // 32kb + 16k2 + 8(t/4) + 4hh + t%4, matching where P sits in the S^T accumulator.
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      bf16x8 vop[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const unsigned char* vp = Vs + (kb * 32 + k2 * 16) * T::ROW_BYTES;
+          vop[kb][k2] = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(vp + voff[db][0]),
+                                         reinterpret_cast<const uint16_t*>(vp + voff[db][1]));
+        }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) acc[db] = mfma32(vop[kb][k2], pb[kb][k2], acc[db]);
+    }
+  };
+
+  // Tile j on stage cur while tile j + 1 loads into nxt; one barrier per tile
+  // for every wave, whichever loop below runs it.
+  auto step = [&](auto masked_tag, int j, const unsigned char* cur, unsigned char* nxt) {
+    if (j + 1 < ntiles) issue(j + 1, nxt);
+    tile(masked_tag, j * kBC, cur);
     wait_loads();
     __syncthreads();
   };
 
+  // Leading tiles lie entirely below this wave's diagonal and inside the
+  // sequence: they run unmasked, two per iteration with fixed stages. The
+  // remaining few tiles (diagonal, ragged end) run one by one.
+  const int n_plain = min(ntiles, (CAUSAL ? min(wrow0 + 1, S) : S) / kBC);
   issue(0, stage0);
   wait_loads();
   __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
-    step(j, stage0, stage1);
-    if (j + 1 < ntiles) step(j + 1, stage1, stage0);
+  int j = 0;
+  for (; j + 2 <= n_plain; j += 2) {
+    step(std::false_type{}, j, stage0, stage1);
+    step(std::false_type{}, j + 1, stage1, stage0);
+  }
+  for (; j < ntiles; ++j) {
+    unsigned char* cur = (j & 1) ? stage1 : stage0;
+    unsigned char* nxt = (j & 1) ? stage0 : stage1;
+    if (j + 1 < ntiles) issue(j + 1, nxt);
+    const int kv0 = j * kBC;
+    if (!CAUSAL || kv0 <= wrow0 + 31) {   // some key of the tile is visible to this wave
+      if (j < n_plain)
+        tile(std::false_type{}, kv0, cur);
+      else
+        tile(std::true_type{}, kv0, cur);
+    }
+    wait_loads();
+    __syncthreads();
   }
 
   const float l_tot = sum_halves(l_run);
