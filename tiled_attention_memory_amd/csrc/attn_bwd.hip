@@ -19,11 +19,12 @@
 //             Delta_i = Delta~_i + c_i is written back for kernel 3. This removes
 //             the error that rounding O to bf16 puts into Delta.
 //   3. dkdv:  key-stationary. One unit = (batch, kv head, 128-key tile, subset
-//             of the group's query heads); 4 waves own 32 keys each and keep
-//             K, V (as MFMA operands) and the dK^T, dV^T accumulators in
-//             registers while 64-row Q/dO tiles stream through LDS. No
-//             atomics: each unit owns its output rows; with more than one
-//             head subset, fp32 partials go to the workspace.
+//             of the group's query heads); 8 waves in pairs own 32 keys per
+//             pair while 64-row Q/dO tiles stream through LDS. In each pair one
+//             wave keeps K and dV^T in registers and computes P, which it hands
+//             to its partner through LDS; the partner keeps V and dK^T, computes
+//             dP and dS. No atomics: each unit owns its output rows; with more
+//             than one head subset, fp32 partials go to the workspace.
 //   4. reduce (only with several subsets): sums the partials in a fixed order.
 // The second operand of every gradient product (P for dV, dS for dK and dQ)
 // enters the bf16 MFMA as a hi + lo pair of bf16 values, so those products
@@ -41,6 +42,7 @@ namespace tam {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBwdThreads = 512;   // dK/dV: 8 waves, two per SIMD
 constexpr int kQBR = 128;   // dq: query rows per workgroup
 constexpr int kQBC = 64;    // dq: keys per tile
 constexpr int kKBC = 128;   // dkdv: keys per workgroup
@@ -129,62 +131,76 @@ struct DkdvArgs {
   TileSched sched;  // streams = (batch*Hkv + kv head) * nsplit + subset; tiles = key tiles
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(DkdvArgs a) {
+// LDS layout of the dK/dV kernel, one array: the two streamed Q/dO stages
+// first (every streamed-tile read is then a per-lane offset plus an immediate
+// below 64 KiB), their lse2/delta rows, and the probabilities one wave of each
+// pair hands to the other.
+template <int D>
+struct DkdvLayout {
   using T = SwzTile<D>;
+  static constexpr int Q0 = 0, DO0 = T::BYTES, Q1 = 2 * T::BYTES, DO1 = 3 * T::BYTES;
+  static constexpr int F0 = 4 * T::BYTES, F1 = F0 + 2 * kKBR * 4;  // lse2[64], delta[64] per stage
+  static constexpr int PB = F1 + 2 * kKBR * 4;                       // P: 4 key blocks x 64 rows x 32 keys fp32
+  static constexpr int PB_BLOCK = kKBR * 32 * 4;
+  static constexpr int BYTES = PB + 4 * PB_BLOCK;
+};
+
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads), amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_kernel(DkdvArgs a) {
+  using T = SwzTile<D>;
+  using L = DkdvLayout<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NLD = T::LOADS / 4;             // 1-KiB loads per wave per tensor per tile
-  constexpr int STAGE = 2 * T::BYTES + 2 * kKBR * 4;  // Q tile, dO tile, lse2[64], delta[64]
-  static_assert(kKBR == T::ROWS, "query tile = LDS tile");
-  __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
+  constexpr int SLD = T::LOADS / 4;             // streamed Q/dO loads per wave per tile
+  static_assert(kKBR == T::ROWS && kKBC == 2 * T::ROWS, "tile sizes");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
 
   int stream, t;
   if (!sched_decode(a.sched, blockIdx.x, &stream, &t)) return;
   const int jt = a.sched.NT - 1 - t;  // key tile; ascending = heaviest first when causal
   const int grp = stream / a.nsplit, sub = stream - grp * a.nsplit;
-  const int b = grp / a.Hkv, kvh = grp - b * a.Hkv;
+  const int b = grp / a.Hkv;
+  const int kvh = grp - b * a.Hkv;
   const int g = a.Hq / a.Hkv;
   const int hps = g / a.nsplit;           // query heads per subset
   const int h_first = kvh * g + sub * hps;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
+  const int kblk = wave & 3;         // this wave's 32 keys within the unit
+  const bool vrole = wave < 4;       // P and dV (with K resident); else dP, dS and dK (with V resident)
   const int col = lane & 31, half = lane >> 5;
   const int S = a.S;
   const size_t kv_base = (size_t)grp * S * D;
   const int kvt0 = jt * kKBC;
-  const int kvb0 = kvt0 + 32 * wave;   // this wave's first key
+  const int kvb0 = kvt0 + 32 * kblk;   // this wave's first key
   const int kvrow = kvb0 + col;        // the key this lane owns
+  const uint32_t lds0 = lds_address(smem);
 
-  // K and V rows as MFMA B operands, resident for the whole unit.
-  bf16x8 kf[KS], vf[KS];
+  // K (for S) or V (for dP) rows of this wave's keys as MFMA B operands.
+  bf16x8 kvf[KS];
   {
-    const size_t off = kv_base + (size_t)kvrow * D + 8 * half;
+    const uint16_t* src = (vrole ? a.k : a.v) + kv_base + (size_t)kvrow * D + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bool in = kvrow < S;
-      kf[ks] = in ? *reinterpret_cast<const bf16x8*>(a.k + off + 16 * ks)
-                  : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-      vf[ks] = in ? *reinterpret_cast<const bf16x8*>(a.v + off + 16 * ks)
-                  : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      kvf[ks] = kvrow < S ? *reinterpret_cast<const bf16x8*>(src + 16 * ks)
+                          : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
 
-  // per-lane LDS offsets, fixed for every tile (see SwzTile)
+  // per-lane LDS offsets, fixed for the whole unit (see SwzTile)
   const int i16 = lane & 15;
   const int dsub = 16 * ((lane >> 4) & 1);
-  int roff[KS], toff[DB][2], loff[NLD];
+  int rr[KS], tt[DB][2];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) roff[ks] = T::chunk_off(col, 2 * ks + half);
+  for (int ks = 0; ks < KS; ++ks) rr[ks] = T::chunk_off(col, 2 * ks + half);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi)
-      toff[db][hi] = T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) loff[i] = T::load_src(wave * NLD + i, lane);
+      tt[db][hi] = T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
+  // this lane's slots of the P hand-off block: element v of 32-row block qs at (16 qs + v) * 64 + lane
+  float* pbuf = reinterpret_cast<float*>(smem + L::PB + kblk * L::PB_BLOCK) + lane;
 
   const int NQ = (S + kKBR - 1) / kKBR;
   const int i_min = CAUSAL ? kvt0 / kKBR : 0;
@@ -196,165 +212,170 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(DkdvArgs a) 
   auto step_head = [&](int st) { return h_first + st / per_head; };
   auto step_tile = [&](int st) { return NQ - 1 - st % per_head; };
 
-  // Q, dO tiles and their lse2, delta rows straight into an LDS stage; rows past S read as zeros.
-  auto issue = [&](int st, unsigned char* stage) {
+  int sld[SLD];
+#pragma unroll
+  for (int i = 0; i < SLD; ++i) sld[i] = T::load_src((wave * SLD + i) % T::LOADS, lane);
+
+  // Q, dO tiles and their lse2, delta rows straight into stage `stg`; rows past S read as zeros.
+  auto issue = [&](int st, int stg) {
     const int hq = step_head(st), row0 = step_tile(st) * kKBR;
     const size_t bh = (size_t)b * a.Hq + hq;
     const int rows_left = S - row0;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + (bh * S + row0) * D, rows_left * D * 2);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + (bh * S + row0) * D, rows_left * D * 2);
-    unsigned char* dst = stage + wave * NLD * 1024;
+    const __amdgpu_buffer_rsrc_t rqd = make_rsrc(a.q + (bh * S + row0) * D, rows_left * D * 2);
+    const __amdgpu_buffer_rsrc_t rdd = make_rsrc(a.dout + (bh * S + row0) * D, rows_left * D * 2);
+    const uint32_t base = lds0 + (stg ? L::Q1 : L::Q0);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      load_lds16(rq, dst + i * 1024, loff[i]);
-      load_lds16(rd, dst + T::BYTES + i * 1024, loff[i]);
+    for (int i = 0; i < SLD; ++i) {
+      const int gi = wave * SLD + i, which = gi / T::LOADS, li = gi % T::LOADS;
+      dma16(which == 0 ? rqd : rdd, base + which * T::BYTES + li * 1024, sld[i]);
     }
     if (wave < 2) {
       const float* src = wave == 0 ? a.lse2 : a.delta;
       const __amdgpu_buffer_rsrc_t rf = make_rsrc(src + bh * S + row0, rows_left * 4);
-      load_lds4(rf, stage + 2 * T::BYTES + wave * kKBR * 4, lane * 4);
+      dma4(rf, lds0 + (stg ? L::F1 : L::F0) + wave * kKBR * 4, lane * 4);
     }
   };
 
-  f32x16 acck[DB], accv[DB];
+  f32x16 acc[DB];   // dV^T (P role) or dK^T (dS role)
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    acck[db] = f32x16{};
-    accv[db] = f32x16{};
-  }
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   const float c = a.c;
 
-  // One 64-row query tile against this wave's 32 keys, as two 32-row blocks.
-  // The products of both blocks are issued before either block's elementwise
-  // work, so one block's VALU work can run under the other's MFMAs. MASKED:
-  // the tile meets the diagonal or the end of the sequence; hidden (query, key)
-  // pairs get P = 0 and blocks entirely before this wave's keys are skipped.
-  auto tile = [&](auto masked_tag, int it, const unsigned char* cur) {
+  // One streamed tile of 64 query rows (two 32-row blocks) against this wave's
+  // 32 keys. MASKED: the tile meets the diagonal of the unit's keys or the end
+  // of the sequence; hidden (query, key) pairs get P = 0 and blocks entirely
+  // before the wave's keys are skipped. The P role computes S and P, hands P to
+  // its partner and accumulates dV; the dS role computes dP, takes P, forms dS
+  // and accumulates dK. The barrier in the middle orders the hand-off.
+  auto tile = [&](auto masked_tag, auto stage_tag, int it) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const unsigned char* Qs = cur;
-    const unsigned char* Ds = cur + T::BYTES;
-    const float* Fs = reinterpret_cast<const float*>(cur + 2 * T::BYTES);
+    constexpr int STG = decltype(stage_tag)::value;
+    constexpr int QB = STG ? L::Q1 : L::Q0, DOB = STG ? L::DO1 : L::DO0, FB = STG ? L::F1 : L::F0;
+    const float* Fs = reinterpret_cast<const float*>(smem + FB);
     bool run[2];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) run[qs] = !(MASKED && CAUSAL && it * kKBR + qs * 32 + 31 < kvb0);
-
-    // S[q][kv] and dP[q][kv]: lane holds key kvrow, rows it*64 + 32qs + 8(v/4) + 4half + v%4
-    f32x16 sc[2], dp[2];
+    // Products over the head dim: S = Q K^T (P role) or dP = dO V^T (dS role);
+    // lane holds key kvrow, rows it*64 + 32qs + 8(v/4) + 4half + v%4.
+    const int AB = vrole ? QB : DOB;
+    f32x16 x[2];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-      sc[qs] = f32x16{};
-      dp[qs] = f32x16{};
+      x[qs] = f32x16{};
       if (!run[qs]) continue;
-      const int rb = qs * 32 * T::ROW_BYTES;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sc[qs] = mfma32(*reinterpret_cast<const bf16x8*>(Qs + rb + roff[ks]), kf[ks], sc[qs]);
-        dp[qs] = mfma32(*reinterpret_cast<const bf16x8*>(Ds + rb + roff[ks]), vf[ks], dp[qs]);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        x[qs] = mfma32(*reinterpret_cast<const bf16x8*>(smem + AB + qs * 32 * T::ROW_BYTES + rr[ks]), kvf[ks],
+                       x[qs]);
     }
-    bf16x8 ph[2][2], pl[2][2], dh[2][2], dl[2][2];
+    bf16x8 hi[2][2], lo[2][2];
+    if (vrole) {
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      float p[16], ds[16];
+      for (int qs = 0; qs < 2; ++qs) {
+        float p[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ql = qs * 32 + 8 * i + 4 * half;   // local row of v = 4i
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(Fs + ql);
-        const f32x4 dlt = *reinterpret_cast<const f32x4*>(Fs + kKBR + ql);
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(Fs + qs * 32 + 8 * i + 4 * half);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int v = 4 * i + r;
-          float e = fast_exp2(fmaf(sc[qs][v], c, -l2[r]));
-          if (MASKED) {
-            const int qrow = it * kKBR + ql + r;
-            const bool ok = qrow < S && kvrow < S && (!CAUSAL || kvrow <= qrow);
-            e = ok ? e : 0.f;
+          for (int r = 0; r < 4; ++r) {
+            const int v = 4 * i + r;
+            float e = fast_exp2(fmaf(x[qs][v], c, -l2[r]));
+            if (MASKED) {
+              const int qrow = it * kKBR + qs * 32 + 8 * i + 4 * half + r;
+              const bool ok = run[qs] && qrow < S && kvrow < S && (!CAUSAL || kvrow <= qrow);
+              e = ok ? e : 0.f;
+            }
+            p[v] = e;
+            pbuf[(16 * qs + v) * 64] = e;
           }
-          p[v] = e;
-          ds[v] = e * (dp[qs][v] - dlt[r]);
         }
-      }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        split_bf16x8(p + 8 * k2, &ph[qs][k2], &pl[qs][k2]);
-        split_bf16x8(ds + 8 * k2, &dh[qs][k2], &dl[qs][k2]);
+        for (int k2 = 0; k2 < 2; ++k2) split_bf16x8(p + 8 * k2, &hi[qs][k2], &lo[qs][k2]);
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS; A operands read transposed from the row-major tiles.
+    __syncthreads();  // P handed over
+    if (!vrole) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        float ds[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 dlt = *reinterpret_cast<const f32x4*>(Fs + kKBR + qs * 32 + 8 * i + 4 * half);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int v = 4 * i + r;
+            ds[v] = pbuf[(16 * qs + v) * 64] * (x[qs][v] - dlt[r]);
+          }
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) split_bf16x8(ds + 8 * k2, &hi[qs][k2], &lo[qs][k2]);
+      }
+    }
+    // dV^T += dO^T P (P role) or dK^T += Q^T dS (dS role); the A operand is read
+    // transposed from the other streamed tile.
+    const int TB = vrole ? DOB : QB;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       if (!run[qs]) continue;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int ro = (qs * 32 + k2 * 16) * T::ROW_BYTES;
-          const bf16x8 a_do = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(Ds + ro + toff[db][0]),
-                                               reinterpret_cast<const uint16_t*>(Ds + ro + toff[db][1]));
-          const bf16x8 a_q = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(Qs + ro + toff[db][0]),
-                                              reinterpret_cast<const uint16_t*>(Qs + ro + toff[db][1]));
-          accv[db] = mfma32(a_do, ph[qs][k2], accv[db]);
-          accv[db] = mfma32(a_do, pl[qs][k2], accv[db]);
-          acck[db] = mfma32(a_q, dh[qs][k2], acck[db]);
-          acck[db] = mfma32(a_q, dl[qs][k2], acck[db]);
+        for (int db = 0; db < DB; ++db) {
+          const int ro = TB + (qs * 32 + k2 * 16) * T::ROW_BYTES;
+          const bf16x8 at = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(smem + ro + tt[db][0]),
+                                             reinterpret_cast<const uint16_t*>(smem + ro + tt[db][1]));
+          acc[db] = mfma32(at, hi[qs][k2], acc[db]);
+          acc[db] = mfma32(at, lo[qs][k2], acc[db]);
         }
     }
   };
 
-  auto step = [&](int st, const unsigned char* cur, unsigned char* nxt) {
-    if (st + 1 < nsteps) issue(st + 1, nxt);
+  auto step = [&](auto stage_tag, int st) {
+    constexpr int STG = decltype(stage_tag)::value;
+    if (st + 1 < nsteps) issue(st + 1, STG ^ 1);
     const int it = step_tile(st);
     // the whole workgroup takes the same branch: the tile meets the diagonal of
     // the unit's 128 keys, or the end of the sequence
     const bool masked = (CAUSAL && it * kKBR < kvt0 + kKBC) || it * kKBR + kKBR > S || kvt0 + kKBC > S;
     if (masked)
-      tile(std::true_type{}, it, cur);
+      tile(std::true_type{}, stage_tag, it);
     else
-      tile(std::false_type{}, it, cur);
+      tile(std::false_type{}, stage_tag, it);
     wait_loads();
     __syncthreads();
   };
 
-  if (nsteps > 0) issue(0, stage0);
+  if (nsteps > 0) issue(0, 0);
   wait_loads();
   __syncthreads();
   for (int st = 0; st < nsteps; st += 2) {
-    step(st, stage0, stage1);
-    if (st + 1 < nsteps) step(st + 1, stage1, stage0);
+    step(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < nsteps) step(std::integral_constant<int, 1>{}, st + 1);
   }
 
   // lane holds key kvrow, head-dim entries 32db + 8i + 4half + (0..3)
   if (kvrow < S) {
+    const float mul = vrole ? 1.f : a.scale;
     if (a.nsplit == 1) {
-      uint16_t* kp = a.dk + kv_base + (size_t)kvrow * D + 4 * half;
-      uint16_t* vp = a.dv + kv_base + (size_t)kvrow * D + 4 * half;
+      uint16_t* op = (vrole ? a.dv : a.dk) + kv_base + (size_t)kvrow * D + 4 * half;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x16& K = acck[db];
-          const f32x16& V = accv[db];
-          u32x2 wk = {pack_bf16(K[4 * i] * a.scale, K[4 * i + 1] * a.scale),
-                      pack_bf16(K[4 * i + 2] * a.scale, K[4 * i + 3] * a.scale)};
-          u32x2 wv = {pack_bf16(V[4 * i], V[4 * i + 1]), pack_bf16(V[4 * i + 2], V[4 * i + 3])};
-          *reinterpret_cast<u32x2*>(kp + 32 * db + 8 * i) = wk;
-          *reinterpret_cast<u32x2*>(vp + 32 * db + 8 * i) = wv;
+          const f32x16& A = acc[db];
+          u32x2 w = {pack_bf16(A[4 * i] * mul, A[4 * i + 1] * mul), pack_bf16(A[4 * i + 2] * mul, A[4 * i + 3] * mul)};
+          *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i) = w;
         }
     } else {
       const size_t total = (size_t)(a.sched.BH / a.nsplit) * S * D;  // B*Hkv*S*D
-      float* kp = a.part + ((size_t)sub * 2) * total + kv_base + (size_t)kvrow * D + 4 * half;
-      float* vp = kp + total;
+      float* op = a.part + ((size_t)sub * 2 + (vrole ? 1 : 0)) * total + kv_base + (size_t)kvrow * D + 4 * half;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x16& K = acck[db];
-          const f32x16& V = accv[db];
-          f32x4 wk = {K[4 * i] * a.scale, K[4 * i + 1] * a.scale, K[4 * i + 2] * a.scale,
-                      K[4 * i + 3] * a.scale};
-          f32x4 wv = {V[4 * i], V[4 * i + 1], V[4 * i + 2], V[4 * i + 3]};
-          *reinterpret_cast<f32x4*>(kp + 32 * db + 8 * i) = wk;
-          *reinterpret_cast<f32x4*>(vp + 32 * db + 8 * i) = wv;
+          const f32x16& A = acc[db];
+          f32x4 w = {A[4 * i] * mul, A[4 * i + 1] * mul, A[4 * i + 2] * mul, A[4 * i + 3] * mul};
+          *reinterpret_cast<f32x4*>(op + 32 * db + 8 * i) = w;
         }
     }
   }
@@ -524,16 +545,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(DqArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int ro = (kb * 32 + k2 * 16) * T::ROW_BYTES;
+        bf16x8 a_k[DB];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int ro = (kb * 32 + k2 * 16) * T::ROW_BYTES;
-          const bf16x8 a_k = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][0]),
-                                              reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][1]));
-          acc[db] = mfma32(a_k, dh[kb][k2], acc[db]);
-          acc[db] = mfma32(a_k, dl[kb][k2], acc[db]);
-          accpk[db] = mfma32(a_k, ph[kb][k2], accpk[db]);
+        for (int db = 0; db < DB; ++db)
+          a_k[db] = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][0]),
+                                     reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][1]));
+        // 2 * DB independent accumulator chains; consecutive MFMAs use different ones
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          acc[db] = mfma32(a_k[db], dh[kb][k2], acc[db]);
+          accpk[db] = mfma32(a_k[db], ph[kb][k2], accpk[db]);
         }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], dl[kb][k2], acc[db]);
+      }
   };
 
   auto step = [&](int j, const unsigned char* cur, unsigned char* nxt) {
@@ -645,7 +672,7 @@ hipError_t launch_all(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
     a.sched.chunk = (a.sched.BH + 7) / 8;
     void* args[] = {&a};
     e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL>),
-                        dim3((unsigned)sched_grid(a.sched)), dim3(kThreads), args, 0, stream);
+                        dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
     if (e != hipSuccess || (e = mark(3)) != hipSuccess) return e;
   }
   if (w.nsplit > 1) {  // 4. fixed-order sum of the head-subset partials

@@ -179,6 +179,33 @@ __device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, void* lds_ba
                                            voffset, 0, 0, 0);
 }
 
+// The same 16-byte direct load, issued as inline assembly for kernels that keep
+// every LDS buffer in one array: the compiler then does not treat the bytes it
+// writes as aliasing later LDS reads of other parts of that array (which would
+// make it wait for the load before those reads). Such kernels wait for their
+// loads with wait_loads() and a barrier before reading the written bytes.
+// lds_addr is the byte address in LDS (the same for the whole wave).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voffset), "s"(r)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voffset), "s"(r)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address of a generic pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+
 // Wait until this wave's outstanding global loads (including loads into LDS) are done.
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

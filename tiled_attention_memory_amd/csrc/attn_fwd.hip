@@ -145,16 +145,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     const unsigned char* Vs = cur + T::BYTES;
 
     // S^T for two 32-key blocks: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow.
+    // two independent accumulator chains, interleaved
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 kop[KS];
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kop[ks] = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * T::ROW_BYTES + koff[ks]);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[kb] = mfma32(kop[ks], qf[ks], s[kb]);
-    }
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + kb * 32 * T::ROW_BYTES + koff[ks]), qf[ks], s[kb]);
 
     // key of accumulator element v of block kb, and whether this row may see it
     auto visible = [&](int kb, int v) {
@@ -210,22 +207,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     // O^T += V^T P^T: the k index of MFMA (kb, k2) slot t of lane half hh is key
     // 32kb + 16k2 + 8(t/4) + 4hh + t%4, matching where P sits in the S^T accumulator.
+    // the DB accumulators form independent chains: head-dim block innermost
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      bf16x8 vop[2][2];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const unsigned char* vp = Vs + (kb * 32 + k2 * 16) * T::ROW_BYTES;
+        bf16x8 vop[DB];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const unsigned char* vp = Vs + (kb * 32 + k2 * 16) * T::ROW_BYTES;
-          vop[kb][k2] = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(vp + voff[db][0]),
-                                         reinterpret_cast<const uint16_t*>(vp + voff[db][1]));
-        }
+        for (int db = 0; db < DB; ++db)
+          vop[db] = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(vp + voff[db][0]),
+                                     reinterpret_cast<const uint16_t*>(vp + voff[db][1]));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) acc[db] = mfma32(vop[kb][k2], pb[kb][k2], acc[db]);
-    }
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32(vop[db], pb[kb][k2], acc[db]);
+      }
   };
 
   // Tile j on stage cur while tile j + 1 loads into nxt; one barrier per tile
