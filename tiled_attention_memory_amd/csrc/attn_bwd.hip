@@ -42,7 +42,7 @@ namespace tam {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBwdThreads = 512;   // dK/dV: 8 waves, two per SIMD
+constexpr int kBwdThreads = 512;   // dQ and dK/dV: 8 waves, two per SIMD
 constexpr int kQBR = 128;   // dq: query rows per workgroup
 constexpr int kQBC = 64;    // dq: keys per tile
 constexpr int kKBC = 128;   // dkdv: keys per workgroup
@@ -416,22 +416,36 @@ struct DqArgs {
   TileSched sched;
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(DqArgs a) {
+// LDS layout of the dQ kernel: two stages of K and V tiles, then the
+// probabilities one wave of each pair hands to the other.
+template <int D>
+struct DqLayout {
   using T = SwzTile<D>;
+  static constexpr int K0 = 0, V0 = T::BYTES, K1 = 2 * T::BYTES, V1 = 3 * T::BYTES;
+  static constexpr int PB = 4 * T::BYTES;
+  static constexpr int PB_BLOCK = 32 * kQBC * 4;  // 32 rows x 64 keys fp32
+  static constexpr int BYTES = PB + 4 * PB_BLOCK;
+  static_assert(4 * (D / 32) * 16 * 64 * 4 <= PB, "final hand-off fits in the stages");
+};
+
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads), amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(DqArgs a) {
+  using T = SwzTile<D>;
+  using L = DqLayout<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NLD = T::LOADS / 4;
-  constexpr int STAGE = 2 * T::BYTES;   // K tile then V tile
-  static_assert(kQBC == T::ROWS, "key tile = LDS tile");
-  __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
+  constexpr int NLD = T::LOADS / 4;   // K and V loads per wave per tile
+  static_assert(kQBC == T::ROWS && kQBR == 128, "tile sizes");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
 
   int bh, qt;
   if (!sched_decode(a.sched, blockIdx.x, &bh, &qt)) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
+  const int rblk = wave & 3;         // this pair's 32 query rows within the unit
+  const bool prole = wave < 4;       // S, P and P K (with Q resident); else dP, dS and dQ (with dO resident)
   const int col = lane & 31, half = lane >> 5;
   const int S = a.S;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
@@ -440,23 +454,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(DqArgs a) {
   const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
   const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
   const int q0 = qt * kQBR;
-  const int wrow0 = q0 + wave * 32;
+  const int wrow0 = q0 + rblk * 32;
   const int qrow = wrow0 + col;
+  const uint32_t lds0 = lds_address(smem);
 
-  bf16x8 qf[KS], df[KS];
+  // Q (for S) or dO (for dP) rows of this pair's queries as MFMA B operands.
+  bf16x8 xf[KS];
   {
-    const size_t off = q_base + (size_t)qrow * D + 8 * half;
+    const uint16_t* src = (prole ? a.q : a.dout) + q_base + (size_t)qrow * D + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bool in = qrow < S;
-      qf[ks] = in ? *reinterpret_cast<const bf16x8*>(a.q + off + 16 * ks)
-                  : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-      df[ks] = in ? *reinterpret_cast<const bf16x8*>(a.dout + off + 16 * ks)
-                  : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      xf[ks] = qrow < S ? *reinterpret_cast<const bf16x8*>(src + 16 * ks)
+                        : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
-  const float l2row = qrow < S ? a.lse2[(size_t)bh * S + qrow] : 0.f;
-  const float drow = qrow < S ? a.delta[(size_t)bh * S + qrow] : 0.f;
+  const float rowval = qrow < S ? (prole ? a.lse2 : a.delta)[(size_t)bh * S + qrow] : 0.f;  // lse2 or Delta~
 
   // per-lane LDS offsets, fixed for every tile (see SwzTile)
   const int i16 = lane & 15;
@@ -470,122 +481,167 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(DqArgs a) {
     for (int hi = 0; hi < 2; ++hi)
       toff[db][hi] = T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) loff[i] = T::load_src(wave * NLD + i, lane);
+  for (int i = 0; i < NLD; ++i) loff[i] = T::load_src((wave * NLD + i) % T::LOADS, lane);
+  // this lane's slots of the P hand-off block: key v of 32-key block kb at (16 kb + v) * 64 + lane
+  float* pbuf = reinterpret_cast<float*>(smem + L::PB + rblk * L::PB_BLOCK) + lane;
 
   const int last_row = min(q0 + kQBR, S) - 1;
   const int n_kv = (S + kQBC - 1) / kQBC;
   const int ntiles = CAUSAL ? min(n_kv, last_row / kQBC + 1) : n_kv;
 
-  auto issue = [&](int j, unsigned char* stage) {
+  // K and V tiles straight into stage `stg`; rows past S read as zeros.
+  auto issue = [&](int j, int stg) {
     const int row0 = j * kQBC;
     const int bytes = (S - row0) * D * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)row0 * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)row0 * D, bytes);
-    unsigned char* dst = stage + wave * NLD * 1024;
+    const uint32_t base = lds0 + (stg ? L::K1 : L::K0);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      load_lds16(rk, dst + i * 1024, loff[i]);
-      load_lds16(rv, dst + T::BYTES + i * 1024, loff[i]);
+      const int gi = wave * NLD + i, which = gi / T::LOADS, li = gi % T::LOADS;
+      dma16(which == 0 ? rk : rv, base + which * T::BYTES + li * 1024, loff[i]);
     }
   };
 
-  f32x16 acc[DB], accpk[DB];  // dQ^T with Delta~, and (P K)^T for the exact-Delta correction
+  f32x16 acc[DB];  // (P K)^T (P role) or dQ^T with Delta~ (dS role)
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    acc[db] = f32x16{};
-    accpk[db] = f32x16{};
-  }
-  float csum = 0.f;  // this lane's half of c = sum_j dS~_j for its row
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float csum = 0.f;  // dS role: this lane's half of c = sum_j dS~_j for its row
   const float c = a.c;
 
-  // One 64-key tile as two 32-key blocks; the products of both blocks are
-  // issued before either block's elementwise work. MASKED: the tile meets this
-  // wave's diagonal or the end of the sequence.
-  auto tile = [&](auto masked_tag, int kv0, const unsigned char* cur) {
+  // One 64-key tile as two 32-key blocks against this pair's 32 rows. MASKED:
+  // the tile meets the pair's diagonal or the end of the sequence; hidden
+  // pairs get P = 0. The P role computes S and P, hands P over and accumulates
+  // P K; the dS role computes dP, takes P, forms dS~ and accumulates dS~ K. The
+  // barrier in the middle orders the hand-off; every wave reaches it.
+  //
+  // S^T = K Q^T or dP^T = V dO^T: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow.
+  auto scores = [&](int AB, f32x16 (&x)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) x[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        x[kb] = mfma32(*reinterpret_cast<const bf16x8*>(smem + AB + kb * 32 * T::ROW_BYTES + roff[ks]), xf[ks], x[kb]);
+  };
+  // K^T rows kb*32 + k2*16 .. +15 of the tile as A operands, read transposed
+  auto kt_operands = [&](int KB, int kb, int k2, bf16x8 (&a_k)[DB]) {
+    const int ro = KB + (kb * 32 + k2 * 16) * T::ROW_BYTES;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      a_k[db] = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(smem + ro + toff[db][0]),
+                                 reinterpret_cast<const uint16_t*>(smem + ro + toff[db][1]));
+  };
+
+  auto tile_p = [&](auto masked_tag, auto stage_tag, int kv0, bool active) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const unsigned char* Ks = cur;
-    const unsigned char* Vs = cur + T::BYTES;
-    // S^T and dP^T for 32 keys: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow
-    f32x16 sc[2], dp[2];
+    constexpr int KB = decltype(stage_tag)::value ? L::K1 : L::K0;
+    bf16x8 ph[2][2];
+    if (active) {
+      f32x16 x[2];
+      scores(KB, x);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sc[kb] = f32x16{};
-      dp[kb] = f32x16{};
-      const int rb = kb * 32 * T::ROW_BYTES;
+      for (int kb = 0; kb < 2; ++kb) {
+        float pf[16];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + rb + roff[ks]), qf[ks], sc[kb]);
-        dp[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Vs + rb + roff[ks]), df[ks], dp[kb]);
-      }
-    }
-    bf16x8 dh[2][2], dl[2][2], ph[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float ds[16], pf[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float e = fast_exp2(fmaf(sc[kb][v], c, -l2row));
-        if (MASKED) {
-          const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          const bool ok = kv < S && (!CAUSAL || kv <= qrow);
-          e = ok ? e : 0.f;
+        for (int v = 0; v < 16; ++v) {
+          float e = fast_exp2(fmaf(x[kb][v], c, -rowval));
+          if (MASKED) {
+            const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+            const bool ok = kv < S && (!CAUSAL || kv <= qrow);
+            e = ok ? e : 0.f;
+          }
+          pf[v] = e;
+          pbuf[(16 * kb + v) * 64] = e;
         }
-        pf[v] = e;
-        ds[v] = e * (dp[kb][v] - drow);
-        csum += ds[v];
-      }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        split_bf16x8(ds + 8 * k2, &dh[kb][k2], &dl[kb][k2]);
-        ph[kb][k2] = pack_bf16x8(pf + 8 * k2);
+        for (int k2 = 0; k2 < 2; ++k2) ph[kb][k2] = pack_bf16x8(pf + 8 * k2);
       }
     }
-    // dQ^T += K^T dS~^T (hi and lo parts) and (PK)^T += K^T P^T: K read transposed
-    // from its row-major tile once for all three products.
+    __syncthreads();  // P handed over
+    if (!active) return;
+    // (P K)^T += K^T P^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const int ro = (kb * 32 + k2 * 16) * T::ROW_BYTES;
         bf16x8 a_k[DB];
+        kt_operands(KB, kb, k2, a_k);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          a_k[db] = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][0]),
-                                     reinterpret_cast<const uint16_t*>(Ks + ro + toff[db][1]));
-        // 2 * DB independent accumulator chains; consecutive MFMAs use different ones
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          acc[db] = mfma32(a_k[db], dh[kb][k2], acc[db]);
-          accpk[db] = mfma32(a_k[db], ph[kb][k2], accpk[db]);
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], dl[kb][k2], acc[db]);
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], ph[kb][k2], acc[db]);
       }
   };
 
-  auto step = [&](int j, const unsigned char* cur, unsigned char* nxt) {
-    if (j + 1 < ntiles) issue(j + 1, nxt);
+  auto tile_ds = [&](auto stage_tag, bool active) {
+    constexpr int STG = decltype(stage_tag)::value;
+    constexpr int KB = STG ? L::K1 : L::K0, VB = STG ? L::V1 : L::V0;
+    f32x16 x[2];
+    if (active) scores(VB, x);
+    __syncthreads();  // P handed over
+    if (!active) return;
+    // dQ^T += K^T dS~^T, hi and lo parts
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float ds[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        ds[v] = pbuf[(16 * kb + v) * 64] * (x[kb][v] - rowval);
+        csum += ds[v];
+      }
+      bf16x8 dh[2], dl[2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) split_bf16x8(ds + 8 * k2, &dh[k2], &dl[k2]);
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        bf16x8 a_k[DB];
+        kt_operands(KB, kb, k2, a_k);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], dh[k2], acc[db]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], dl[k2], acc[db]);
+      }
+    }
+  };
+
+  auto step = [&](auto stage_tag, int j) {
+    constexpr int STG = decltype(stage_tag)::value;
+    if (j + 1 < ntiles) issue(j + 1, STG ^ 1);
     const int kv0 = j * kQBC;
     const bool active = !CAUSAL || kv0 <= wrow0 + 31;
-    if (active) {
+    if (prole) {
+      // uniform per wave: the tile meets the pair's diagonal or the end of the sequence
       const bool masked = (kv0 + kQBC > S) || (CAUSAL && kv0 + kQBC - 1 > wrow0);
       if (masked)
-        tile(std::true_type{}, kv0, cur);
+        tile_p(std::true_type{}, stage_tag, kv0, active);
       else
-        tile(std::false_type{}, kv0, cur);
+        tile_p(std::false_type{}, stage_tag, kv0, active);
+    } else {
+      tile_ds(stage_tag, active);
     }
     wait_loads();
     __syncthreads();
   };
 
-  issue(0, stage0);
+  issue(0, 0);
   wait_loads();
   __syncthreads();
   for (int j = 0; j < ntiles; j += 2) {
-    step(j, stage0, stage1);
-    if (j + 1 < ntiles) step(j + 1, stage1, stage0);
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
+  // P K goes to the dS role through the (now idle) stages: element v of
+  // accumulator db of lane l at float (16 db + v) * 64 + l of the pair's block.
+  float* hand = reinterpret_cast<float*>(smem) + rblk * (DB * 16 * 64) + lane;
+  if (prole) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) hand[(16 * db + v) * 64] = acc[db][v];
+  }
+  __syncthreads();
+  if (prole) return;
   const float corr = sum_halves(csum);  // Delta_i - Delta~_i
   if (qrow < S) {
     uint16_t* op = a.dq + q_base + (size_t)qrow * D + 4 * half;
@@ -595,11 +651,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(DqArgs a) {
       for (int i = 0; i < 4; ++i) {
         float gq[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) gq[r] = a.scale * fmaf(-corr, accpk[db][4 * i + r], acc[db][4 * i + r]);
+        for (int r = 0; r < 4; ++r)
+          gq[r] = a.scale * fmaf(-corr, hand[(16 * db + 4 * i + r) * 64], acc[db][4 * i + r]);
         u32x2 w = {pack_bf16(gq[0], gq[1]), pack_bf16(gq[2], gq[3])};
         *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i) = w;
       }
-    if (half == 0) a.delta[(size_t)bh * S + qrow] = drow + corr;
+    if (half == 0) a.delta[(size_t)bh * S + qrow] = rowval + corr;
   }
 }
 
@@ -647,7 +704,7 @@ hipError_t launch_all(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
     a.sched.chunk = (a.sched.BH + 7) / 8;
     void* args[] = {&a};
     e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL>),
-                        dim3((unsigned)sched_grid(a.sched)), dim3(kThreads), args, 0, stream);
+                        dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
     if (e != hipSuccess || (e = mark(2)) != hipSuccess) return e;
   }
   {  // 3. dK/dV
