@@ -90,6 +90,18 @@ def measured_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def alg_bytes(w):
+    """Bytes the method itself must move, each tensor once: forward reads Q, K, V and
+    writes O and LSE; backward reads Q, K, V, O, dO and LSE, writes Delta once and
+    reads it twice, and writes dQ, dK and dV."""
+    q = w.B * w.Hq * w.S * w.D * 2
+    kv = w.B * w.Hkv * w.S * w.D * 2
+    rows = w.B * w.Hq * w.S * 4
+    fwd = q + 2 * kv + q + rows
+    bwd = 3 * q + 2 * kv + rows + 3 * rows + q + 2 * kv
+    return fwd, bwd
+
+
 def cpu_baseline(w, x, n_groups):
     """The fp64 oracle, untuned, on a bounded sample: whole GQA groups of the same workload."""
     import numpy as np
@@ -120,6 +132,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2_70b_layer_s4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
+                    help="before each step, overwrite a MIB-mebibyte buffer so that L2 and the "
+                         "memory-side cache start cold (for the short, bandwidth-bound shapes); "
+                         "the step time is then the sum of the per-kernel event times")
     ap.add_argument("--cpu-groups", type=int, default=8)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy a MIB-mebibyte device buffer 3 times (a plain copy "
@@ -171,11 +187,15 @@ def main():
     ev_b = [(ctypes.c_void_p * tam.BWD_EVENTS)(*[hip.event() for _ in range(tam.BWD_EVENTS)])
             for _ in range(K)]
     e0, e1 = hip.event(), hip.event()
+    flush = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda")
+             if args.flush_mib else None)
     log(f"[bench] {args.warmup} warmup steps done; timing {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     hip.record(e0, sh)
     for i in range(K):
+        if flush is not None:
+            flush.fill_(float(i))
         step(ev_f[i], ev_b[i])
     hip.record(e1, sh)
     torch.cuda.synchronize()
@@ -192,6 +212,7 @@ def main():
         "attn_bwd_dkdv_kernel": avg([(e[2], e[3]) for e in ev_b]),
         "attn_bwd_reduce_kernel": avg([(e[3], e[4]) for e in ev_b]),
     }
+    bwd_ms = avg([(e[0], e[4]) for e in ev_b])
     for a, b in ev_f:
         hip.destroy(a)
         hip.destroy(b)
@@ -199,7 +220,8 @@ def main():
         for j in range(tam.BWD_EVENTS):
             hip.destroy(e[j])
 
-    ms_step = total_ms / K
+    # with flushing, the timed region also holds the fills: use the kernels' own events
+    ms_step = total_ms / K if flush is None else per["attn_fwd_kernel"] + bwd_ms
     flops = w.fwd_flops() + w.bwd_flops()
     value = flops / (ms_step * 1e-3) / 1e12
     # Algorithmic FLOPs each kernel carries out of the counted total: the forward
@@ -249,7 +271,10 @@ def main():
                    "causal": True, "global_batch": w.B, "seq_len": w.S, "parallelism": "none"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(w.fwd_flops() / (per["attn_fwd_kernel"] * 1e-3) / 1e12, 1),
-        "bwd_tflops": round(w.bwd_flops() / (sum(per[n] for n in per if "bwd" in n) * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),
+        # algorithmic bytes (each tensor once) over the pass time, for the short shapes
+        "fwd_alg_gbps": round(alg_bytes(w)[0] / (per["attn_fwd_kernel"] * 1e-3) / 1e9, 1),
+        "bwd_alg_gbps": round(alg_bytes(w)[1] / (bwd_ms * 1e-3) / 1e9, 1),
         "kernels": kernels,
         "roofline": roofline,
     }

@@ -207,17 +207,19 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   const int per_head = NQ - i_min;       // query tiles visited per head
   const int nsteps = per_head * hps;
 
-  // step -> (query head, query tile); tiles run from the last one down so that
-  // concurrent units of one group read the same Q/dO tiles at the same time.
-  auto step_head = [&](int st) { return h_first + st / per_head; };
-  auto step_tile = [&](int st) { return NQ - 1 - st % per_head; };
+  // step -> (query head, query tile): tiles run from the last one down, the
+  // subset's heads innermost, so that the units resident at the same time
+  // (whatever their key tile) stream the same Q/dO tiles together and share
+  // them in L2.
+  auto step_head = [&](int st) TAM_INLINE { return h_first + st % hps; };
+  auto step_tile = [&](int st) TAM_INLINE { return NQ - 1 - st / hps; };
 
   int sld[SLD];
 #pragma unroll
   for (int i = 0; i < SLD; ++i) sld[i] = T::load_src((wave * SLD + i) % T::LOADS, lane);
 
   // Q, dO tiles and their lse2, delta rows straight into stage `stg`; rows past S read as zeros.
-  auto issue = [&](int st, int stg) {
+  auto issue = [&](int st, int stg) TAM_INLINE {
     const int hq = step_head(st), row0 = step_tile(st) * kKBR;
     const size_t bh = (size_t)b * a.Hq + hq;
     const int rows_left = S - row0;
@@ -247,7 +249,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   // before the wave's keys are skipped. The P role computes S and P, hands P to
   // its partner and accumulates dV; the dS role computes dP, takes P, forms dS
   // and accumulates dK. The barrier in the middle orders the hand-off.
-  auto tile = [&](auto masked_tag, auto stage_tag, int it) {
+  auto tile = [&](auto masked_tag, auto stage_tag, int it) TAM_INLINE {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int STG = decltype(stage_tag)::value;
     constexpr int QB = STG ? L::Q1 : L::Q0, DOB = STG ? L::DO1 : L::DO0, FB = STG ? L::F1 : L::F0;
@@ -330,7 +332,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
     }
   };
 
-  auto step = [&](auto stage_tag, int st) {
+  auto step = [&](auto stage_tag, int st) TAM_INLINE {
     constexpr int STG = decltype(stage_tag)::value;
     if (st + 1 < nsteps) issue(st + 1, STG ^ 1);
     const int it = step_tile(st);
@@ -357,14 +359,19 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   if (kvrow < S) {
     const float mul = vrole ? 1.f : a.scale;
     if (a.nsplit == 1) {
-      uint16_t* op = (vrole ? a.dv : a.dk) + kv_base + (size_t)kvrow * D + 4 * half;
+      uint16_t* op = (vrole ? a.dv : a.dk) + kv_base + (size_t)kvrow * D + 8 * half;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int m = 0; m < 2; ++m) {
           const f32x16& A = acc[db];
-          u32x2 w = {pack_bf16(A[4 * i] * mul, A[4 * i + 1] * mul), pack_bf16(A[4 * i + 2] * mul, A[4 * i + 3] * mul)};
-          *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i) = w;
+          u32x2 w[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int i = 2 * m + t;
+            w[t] = u32x2{pack_bf16(A[4 * i] * mul, A[4 * i + 1] * mul), pack_bf16(A[4 * i + 2] * mul, A[4 * i + 3] * mul)};
+          }
+          *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
         }
     } else {
       const size_t total = (size_t)(a.sched.BH / a.nsplit) * S * D;  // B*Hkv*S*D
@@ -490,7 +497,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
   const int ntiles = CAUSAL ? min(n_kv, last_row / kQBC + 1) : n_kv;
 
   // K and V tiles straight into stage `stg`; rows past S read as zeros.
-  auto issue = [&](int j, int stg) {
+  auto issue = [&](int j, int stg) TAM_INLINE {
     const int row0 = j * kQBC;
     const int bytes = (S - row0) * D * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)row0 * D, bytes);
@@ -516,7 +523,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
   // barrier in the middle orders the hand-off; every wave reaches it.
   //
   // S^T = K Q^T or dP^T = V dO^T: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow.
-  auto scores = [&](int AB, f32x16 (&x)[2]) {
+  auto scores = [&](int AB, f32x16 (&x)[2]) TAM_INLINE {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) x[kb] = f32x16{};
 #pragma unroll
@@ -526,7 +533,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
         x[kb] = mfma32(*reinterpret_cast<const bf16x8*>(smem + AB + kb * 32 * T::ROW_BYTES + roff[ks]), xf[ks], x[kb]);
   };
   // K^T rows kb*32 + k2*16 .. +15 of the tile as A operands, read transposed
-  auto kt_operands = [&](int KB, int kb, int k2, bf16x8 (&a_k)[DB]) {
+  auto kt_operands = [&](int KB, int kb, int k2, bf16x8 (&a_k)[DB]) TAM_INLINE {
     const int ro = KB + (kb * 32 + k2 * 16) * T::ROW_BYTES;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -534,7 +541,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
                                  reinterpret_cast<const uint16_t*>(smem + ro + toff[db][1]));
   };
 
-  auto tile_p = [&](auto masked_tag, auto stage_tag, int kv0, bool active) {
+  auto tile_p = [&](auto masked_tag, auto stage_tag, int kv0, bool active) TAM_INLINE {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int KB = decltype(stage_tag)::value ? L::K1 : L::K0;
     bf16x8 ph[2][2];
@@ -573,7 +580,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
       }
   };
 
-  auto tile_ds = [&](auto stage_tag, bool active) {
+  auto tile_ds = [&](auto stage_tag, bool active) TAM_INLINE {
     constexpr int STG = decltype(stage_tag)::value;
     constexpr int KB = STG ? L::K1 : L::K0, VB = STG ? L::V1 : L::V0;
     f32x16 x[2];
@@ -604,7 +611,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
     }
   };
 
-  auto step = [&](auto stage_tag, int j) {
+  auto step = [&](auto stage_tag, int j) TAM_INLINE {
     constexpr int STG = decltype(stage_tag)::value;
     if (j + 1 < ntiles) issue(j + 1, STG ^ 1);
     const int kv0 = j * kQBC;
@@ -644,17 +651,22 @@ void attn_bwd_dq_kernel(DqArgs a) {
   if (prole) return;
   const float corr = sum_halves(csum);  // Delta_i - Delta~_i
   if (qrow < S) {
-    uint16_t* op = a.dq + q_base + (size_t)qrow * D + 4 * half;
+    uint16_t* op = a.dq + q_base + (size_t)qrow * D + 8 * half;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float gq[4];
+      for (int m = 0; m < 2; ++m) {
+        u32x2 w[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          gq[r] = a.scale * fmaf(-corr, hand[(16 * db + 4 * i + r) * 64], acc[db][4 * i + r]);
-        u32x2 w = {pack_bf16(gq[0], gq[1]), pack_bf16(gq[2], gq[3])};
-        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i) = w;
+        for (int t = 0; t < 2; ++t) {
+          const int i = 2 * m + t;
+          float gq[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            gq[r] = a.scale * fmaf(-corr, hand[(16 * db + 4 * i + r) * 64], acc[db][4 * i + r]);
+          w[t] = u32x2{pack_bf16(gq[0], gq[1]), pack_bf16(gq[2], gq[3])};
+        }
+        *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
       }
     if (half == 0) a.delta[(size_t)bh * S + qrow] = rowval + corr;
   }

@@ -20,6 +20,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+// Kernel bodies are written with local lambdas; every one of them must be
+// inlined, or its captured register arrays would be spilled to scratch memory.
+#define TAM_INLINE __attribute__((always_inline))
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -58,6 +62,17 @@ __device__ __forceinline__ void swap_halves(float x, float* lo_half, float* hi_h
   auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
   *lo_half = __builtin_bit_cast(float, (uint32_t)r[0]);
   *hi_half = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Store helper for accumulator rows: lanes l and l + 32 each hold 4 values of
+// the same output row, x for columns [8i, 8i+4) + 4 * half and y for columns
+// [8i+8, 8i+12) + 4 * half, as two packed 32-bit pairs. After the exchange the
+// lower half holds columns 8i..8i+7 and the upper half 8i+8..8i+15 of that
+// row, so one 16-byte store per lane covers 32 contiguous bytes per row.
+__device__ __forceinline__ u32x4 pair_halves(u32x2 x, u32x2 y) {
+  auto r0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+  auto r1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+  return u32x4{(uint32_t)r0[0], (uint32_t)r1[0], (uint32_t)r0[1], (uint32_t)r1[1]};
 }
 
 __device__ __forceinline__ float max_halves(float x) {
@@ -209,26 +224,34 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // Wait until this wave's outstanding global loads (including loads into LDS) are done.
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Scheduler shared by the query-tile kernels: work unit = (query head, query
-// tile). Workgroup i runs on XCD i % 8; XCD x owns a contiguous range of
-// heads (so the heads of one key/value group share that XCD's L2) and walks
-// its units from the last query tile to the first, i.e. heaviest first under
-// a causal mask.
+// Scheduler shared by the kernels: work unit = (stream, tile), a stream being
+// a query head or a (key/value head, head subset) pair. Workgroup i runs on
+// XCD i % 8. When the streams divide evenly over the 8 XCDs, XCD x owns a
+// contiguous range of them (so the heads of one key/value group share that
+// XCD's L2) and walks its units from the last tile to the first, i.e.
+// heaviest first under a causal mask for the query-tile kernels. Otherwise
+// the units are dealt out in one global heaviest-first order, so no XCD sits
+// idle when there are fewer than 8 streams or a remainder.
 struct TileSched {
-  int BH;      // B * Hq
-  int NT;      // query tiles per head
-  int chunk;   // heads per XCD: ceil(BH / 8)
+  int BH;      // streams
+  int NT;      // tiles per stream
+  int chunk;   // streams per XCD: ceil(BH / 8)
 };
-
 __host__ __device__ inline long long sched_grid(const TileSched& s) {
-  return 8LL * s.chunk * s.NT;
+  return s.BH % 8 == 0 ? 8LL * s.chunk * s.NT : (long long)s.BH * s.NT;
 }
 
-__device__ __forceinline__ bool sched_decode(const TileSched& s, int bid, int* bh, int* qt) {
+__host__ __device__ inline bool sched_decode(const TileSched& s, int bid, int* bh, int* qt) {
+  if (s.BH % 8 != 0) {
+    if (bid >= s.BH * s.NT) return false;
+    *qt = s.NT - 1 - bid / s.BH;
+    *bh = bid % s.BH;
+    return true;
+  }
   const int x = bid & 7, slot = bid >> 3;
   const int h0 = x * s.chunk;
-  const int hn = min(s.chunk, s.BH - h0);
-  if (hn <= 0 || slot >= hn * s.NT) return false;
+  const int hn = s.chunk;
+  if (slot >= hn * s.NT) return false;
   *qt = s.NT - 1 - slot / hn;
   *bh = h0 + slot % hn;
   return true;

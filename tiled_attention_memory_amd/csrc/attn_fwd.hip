@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int ntiles = CAUSAL ? min(n_kv, last_row / kBC + 1) : n_kv;
 
   // K and V tile j straight into an LDS stage; rows past S read as zeros.
-  auto issue = [&](int j, unsigned char* stage) {
+  auto issue = [&](int j, unsigned char* stage) TAM_INLINE {
     const int row0 = j * kBC;
     const int bytes = (S - row0) * D * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)row0 * D, bytes);
@@ -136,37 +136,43 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   float m_run = -INFINITY;  // running (lazy) max of this row's base-2 scaled scores
   float l_run = 0.f;        // running sum of this lane's half of the row
 
-  // One 64-key tile. MASKED: the tile straddles the diagonal or the end of the
-  // sequence for this wave, so scores of hidden keys are excluded; every other
-  // tile runs without any per-element test.
-  auto tile = [&](auto masked_tag, int kv0, const unsigned char* cur) {
+  // Key blocks KB0 .. KB0 + NKB - 1 (32 keys each) of a 64-key tile. MASKED:
+  // the tile straddles the diagonal or the end of the sequence for this wave,
+  // so scores of hidden keys are excluded; such tiles run one 32-key block at
+  // a time, which keeps fewer scores live. Every other tile runs both blocks
+  // without any per-element test.
+  auto tile = [&](auto masked_tag, auto kb0_tag, auto nkb_tag, int kv0, const unsigned char* cur) TAM_INLINE {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const unsigned char* Ks = cur;
-    const unsigned char* Vs = cur + T::BYTES;
+    constexpr int KB0 = decltype(kb0_tag)::value;
+    constexpr int NKB = decltype(nkb_tag)::value;
+    const unsigned char* Ks = cur + KB0 * 32 * T::ROW_BYTES;
+    const unsigned char* Vs = cur + T::BYTES + KB0 * 32 * T::ROW_BYTES;
 
-    // S^T for two 32-key blocks: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow.
-    // two independent accumulator chains, interleaved
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    // S^T for the 32-key blocks: lane holds keys kv0 + 32(KB0 + kb) + 8(v/4) + 4half + v%4
+    // of row qrow; independent accumulator chains, interleaved
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
         s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + kb * 32 * T::ROW_BYTES + koff[ks]), qf[ks], s[kb]);
 
-    // key of accumulator element v of block kb, and whether this row may see it
-    auto visible = [&](int kb, int v) {
-      const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-      return kv < S && (!CAUSAL || kv <= qrow);
-    };
+    // Whether this row may see the key of accumulator element v of block kb:
+    // that key is kv0 + 32 KB0 + 4half + off with the constant
+    // off = 32kb + 8(v/4) + v%4, so one compare against a per-lane limit decides it.
+    const int lim = (CAUSAL ? min(qrow, S - 1) : S - 1) - (kv0 + 32 * KB0 + 4 * half);
+    auto visible = [&](int kb, int v) TAM_INLINE { return kb * 32 + 8 * (v >> 2) + (v & 3) <= lim; };
     if (MASKED) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[kb][v] = visible(kb, v) ? s[kb][v] : -INFINITY;
     }
     float ext = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) ext = fmaxf(ext, s[kb][v]);
     ext = max_halves(ext);
@@ -174,7 +180,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     // c == 0; neither moves the running max.
     const float mt = ext * c;
     const bool grow = mt > m_run + kLazyMax;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
+    // The few masked tiles rescale unconditionally: a branch here would make
+    // the compiler copy the accumulators and spill.
+    if (MASKED || __builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? mt : m_run;
       const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, 1 where unchanged
       m_run = m_new;
@@ -183,22 +191,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
     }
 
-    float p[2][16];
+    float p[NKB][16];
     float lsum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float e = fast_exp2(fmaf(s[kb][v], c, -m_run));
-        if (MASKED) e = visible(kb, v) ? e : 0.f;  // also covers c == 0, where -inf * c is NaN
+        // hidden scores hold -inf: exp2 gives 0, or NaN when c == 0; both become 0
+        if (MASKED) e = s[kb][v] == -INFINITY ? 0.f : e;
         p[kb][v] = e;
         lsum += e;
       }
     l_run += lsum;
 
-    bf16x8 pb[2][2];
+    bf16x8 pb[NKB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) pb[kb][k2] = pack_bf16x8(&p[kb][8 * k2]);
 
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     // 32kb + 16k2 + 8(t/4) + 4hh + t%4, matching where P sits in the S^T accumulator.
     // the DB accumulators form independent chains: head-dim block innermost
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         const unsigned char* vp = Vs + (kb * 32 + k2 * 16) * T::ROW_BYTES;
@@ -225,9 +234,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 
   // Tile j on stage cur while tile j + 1 loads into nxt; one barrier per tile
   // for every wave, whichever loop below runs it.
-  auto step = [&](auto masked_tag, int j, const unsigned char* cur, unsigned char* nxt) {
+  auto step = [&](auto masked_tag, int j, const unsigned char* cur, unsigned char* nxt) TAM_INLINE {
     if (j + 1 < ntiles) issue(j + 1, nxt);
-    tile(masked_tag, j * kBC, cur);
+    tile(masked_tag, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, j * kBC, cur);
     wait_loads();
     __syncthreads();
   };
@@ -244,32 +253,54 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     step(std::false_type{}, j, stage0, stage1);
     step(std::false_type{}, j + 1, stage1, stage0);
   }
-  for (; j < ntiles; ++j) {
-    unsigned char* cur = (j & 1) ? stage1 : stage0;
-    unsigned char* nxt = (j & 1) ? stage0 : stage1;
-    if (j + 1 < ntiles) issue(j + 1, nxt);
-    const int kv0 = j * kBC;
+  // stages stay compile-time constants here too, so LDS addresses fold into
+  // instruction offsets
+  auto tail_step = [&](auto stage_tag, int jj) TAM_INLINE {
+    constexpr int STG = decltype(stage_tag)::value;
+    const unsigned char* cur = STG ? stage1 : stage0;
+    unsigned char* nxt = STG ? stage0 : stage1;
+    if (jj + 1 < ntiles) issue(jj + 1, nxt);
+    const int kv0 = jj * kBC;
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
     if (!CAUSAL || kv0 <= wrow0 + 31) {   // some key of the tile is visible to this wave
-      if (j < n_plain)
-        tile(std::false_type{}, kv0, cur);
-      else
-        tile(std::true_type{}, kv0, cur);
+      if (jj < n_plain) {
+        tile(std::false_type{}, C0{}, C2{}, kv0, cur);
+      } else {
+        tile(std::true_type{}, C0{}, C1{}, kv0, cur);
+        // the second 32-key block, unless this wave sees none of its keys
+        if ((!CAUSAL || kv0 + 32 <= wrow0 + 31) && kv0 + 32 < S) tile(std::true_type{}, C1{}, C1{}, kv0, cur);
+      }
     }
     wait_loads();
     __syncthreads();
+  };
+  for (; j < ntiles; ++j) {
+    if (j & 1)
+      tail_step(std::integral_constant<int, 1>{}, j);
+    else
+      tail_step(std::integral_constant<int, 0>{}, j);
   }
 
   const float l_tot = sum_halves(l_run);
   if (qrow < S) {
     const float inv = 1.f / l_tot;
-    uint16_t* op = a.o + q_base + (size_t)qrow * D + 4 * half;
+    // lane holds columns 32db + 8i + 4half + (0..3); pairs of i are merged
+    // across the halves so each store writes 16 contiguous bytes per lane
+    uint16_t* op = a.o + q_base + (size_t)qrow * D + 8 * half;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 w = {pack_bf16(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv),
-                   pack_bf16(acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i) = w;
+      for (int m = 0; m < 2; ++m) {
+        u32x2 w[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int i = 2 * m + t;
+          w[t] = u32x2{pack_bf16(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv),
+                       pack_bf16(acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv)};
+        }
+        *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
       }
     if (half == 0) a.lse[(size_t)bh * S + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   }
