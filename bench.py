@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 bf16 flop/clk x 2.4 GHz (AMD's 2.5 PFLOP/s dense figure)
 PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.json")
 KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
 
 
@@ -80,7 +80,7 @@ def kernel_source_sha():
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if still current."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload=workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
