@@ -4,3 +4,4 @@ Only tests/, the smoke check and the bench's CPU-baseline leg use this
 package. The HIP library neither imports it nor is imported by it.
 """
 from . import attention  # noqa: F401
+from . import blocks  # noqa: F401
