@@ -1,5 +1,6 @@
-"""C ABI contract on the CPU: the library loads, exports what include/attn.h
-declares, and rejects every invalid argument before touching the GPU.
+"""C ABI contract on the CPU: the library loads, exports what include/attn.h and
+include/attn_block.h declare, and rejects every invalid argument before
+touching the GPU.
 
 Every call below fails validation, and validation happens before any HIP
 call, so none of them launches anything (no GPU is needed or used).
@@ -13,14 +14,14 @@ import pytest
 import tiled_attention_memory_amd as tam
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("attn.h", "attn_block.h")]
 
 A = 1 << 20          # fake, 16-byte aligned, far-apart "device" addresses (never dereferenced)
 GOOD = dict(B=1, Hq=4, Hkv=2, S=128, D=128, causal=1, scale=0.125)
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    src = "\n".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", src, flags=re.M)))
 
@@ -142,3 +143,62 @@ def test_bwd_aliasing():
     assert bwd(ws_size=need, dk=7 * A + 128) == 9          # dk inside dq
     assert bwd(ws_size=need, ws=6 * A, ) == 9              # workspace on lse
     assert bwd(ws_size=need, dv=5 * A) == 9                # dv on dout
+
+
+# ---------------------------------------------------------------------------
+# context-parallel building block (attn_block.h): validation only
+# ---------------------------------------------------------------------------
+def fwd_block(**kw):
+    a = dict(B=1, Hq=4, Hkv=2, Sq=100, Sk=70, D=128, causal=1, q0=0, k0=0, scale=0.125)
+    ptrs = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=8 * A)
+    for key in list(kw):
+        if key in ptrs:
+            ptrs[key] = kw.pop(key)
+    a.update(kw)
+    return tam.load().attn_fwd_block(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], ptrs["lse"], a["B"], a["Hq"],
+                                     a["Hkv"], a["Sq"], a["Sk"], a["D"], a["causal"], a["q0"], a["k0"], a["scale"],
+                                     None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(lse=0), 1),
+    (dict(Sq=0), 2), (dict(Sk=0), 2), (dict(Sk=(1 << 22) + 1), 2), (dict(Hq=3), 2),
+    (dict(D=96), 3), (dict(scale=float("inf")), 4), (dict(k=2 * A + 8), 5), (dict(causal=2), 8),
+    (dict(q0=(1 << 62) + 1), 2), (dict(k0=-(1 << 62) - 1), 2),
+    (dict(o=A + 4096), 9),          # o_part on top of q
+    (dict(lse=4 * A + 100 * 128), 9),  # lse_part inside o_part (o_part is 4*100*128*4 bytes)
+])
+def test_fwd_block_rejects(kw, status):
+    assert fwd_block(**kw) == status
+
+
+def test_merge_rejects():
+    lib = tam.load()
+    arr = ctypes.c_void_p * 2
+    ok = (arr(A, 2 * A), arr(3 * A, 5 * A))
+    assert lib.attn_merge(*ok, 0, 6 * A, 7 * A, 1, 4, 64, 128, None) == 2           # n = 0
+    assert lib.attn_merge(*ok, 17, 6 * A, 7 * A, 1, 4, 64, 128, None) == 2          # n > ATTN_MAX_MERGE
+    assert lib.attn_merge(arr(A, 0), ok[1], 2, 6 * A, 7 * A, 1, 4, 64, 128, None) == 1
+    assert lib.attn_merge(*ok, 2, 6 * A, 7 * A, 1, 4, 64, 96, None) == 3
+    assert lib.attn_merge(*ok, 2, A + 64, 7 * A, 1, 4, 64, 128, None) == 9          # o on top of a part
+    assert lib.attn_merge(arr(A + 4, 2 * A), ok[1], 2, 6 * A, 7 * A, 1, 4, 64, 128, None) == 5
+
+
+def test_block_backward_rejects():
+    lib = tam.load()
+    B, Hq, Hkv, Sq, Sk, D = 1, 4, 2, 64, 96, 128
+    need = tam.attn_bwd_block_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
+    assert need >= tam.attn_bwd_block_workspace_bytes(B, Hq, Hkv, Sq, 32, D)
+    W = 64 * A
+    assert lib.attn_bwd_block_begin(A, 2 * A, 3 * A, W, need - 1, B, Hq, Hkv, Sq, Sk, D, None) == 6
+    assert lib.attn_bwd_block_begin(A, 2 * A, 3 * A, 0, need, B, Hq, Hkv, Sq, Sk, D, None) == 6
+    assert lib.attn_bwd_block_begin(A, 2 * A, 3 * A, A + 256, need, B, Hq, Hkv, Sq, Sk, D, None) == 9
+    assert lib.attn_bwd_block_dq(A, 2 * A, 3 * A, 4 * A, W, need, B, Hq, Hkv, Sq, Sk, D, 3, 0, 0, 0.1, None) == 8
+    assert lib.attn_bwd_block_dq(A, 2 * A, 3 * A, 4 * A, W, need, B, Hq, Hkv, Sq, Sk, D, 1, (1 << 62) + 1, 0, 0.1,
+                                 None) == 2
+    assert lib.attn_bwd_block_dq_end(0, W, need, B, Hq, Hkv, Sq, Sk, D, 0.1, None) == 1
+    assert lib.attn_bwd_block_dq_end(A, W, need, B, Hq, Hkv, Sq, Sk, D, float("nan"), None) == 4
+    assert lib.attn_bwd_block_dkdv(A, 2 * A, 3 * A, 4 * A, 5 * A, 5 * A, W, need, B, Hq, Hkv, Sq, Sk, D, 1, 0, 0,
+                                   0.1, None) == 9    # dk and dv overlap
+    assert lib.attn_bwd_block_dkdv(A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, W, need, B, Hq, Hkv, Sq, Sk + 512, D, 1,
+                                   0, 0, 0.1, None) == 6    # workspace sized for a smaller key block

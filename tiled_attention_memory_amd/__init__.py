@@ -1,6 +1,6 @@
 """Exact causal GQA attention for MI355X (gfx950): HIP kernels behind a C ABI.
 
-The Python names mirror include/attn.h. The library is loaded on first use
+The Python names mirror include/attn.h and include/attn_block.h. The library is loaded on first use
 and every call fails loudly if it is missing; nothing here computes attention.
 """
 from ._binding import (  # noqa: F401
@@ -8,7 +8,15 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     STATUS,
     BWD_EVENTS,
+    MAX_MERGE,
     AttnError,
+    attn_bwd_block_begin,
+    attn_bwd_block_dkdv,
+    attn_bwd_block_dq,
+    attn_bwd_block_dq_end,
+    attn_bwd_block_workspace_bytes,
+    attn_fwd_block,
+    attn_merge,
     attn_bwd,
     attn_bwd_raw,
     attn_bwd_workspace_bytes,

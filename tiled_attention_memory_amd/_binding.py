@@ -1,7 +1,7 @@
 """ctypes binding of libattn.so: argument marshalling only.
 
 Every computation happens in the HIP kernels behind the C ABI declared in
-include/attn.h. PyTorch is used only to own device memory and to provide the
+include/attn.h and include/attn_block.h. PyTorch is used only to own device memory and to provide the
 stream handle. There is no fallback: if the library is missing, every call
 raises.
 """
@@ -22,8 +22,10 @@ STATUS = {
 }
 
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_bwd_workspace_bytes", "attn_status_string",
-           "attn_version")
+           "attn_version", "attn_fwd_block", "attn_merge", "attn_bwd_block_workspace_bytes",
+           "attn_bwd_block_begin", "attn_bwd_block_dq", "attn_bwd_block_dq_end", "attn_bwd_block_dkdv")
 BWD_EVENTS = 5
+MAX_MERGE = 16
 
 _lock = threading.Lock()
 _lib = None
@@ -60,6 +62,17 @@ def load() -> ctypes.CDLL:
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_version.argtypes = []
         lib.attn_version.restype = i
+        ll = ctypes.c_longlong
+        lib.attn_fwd_block.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, ll, ll, f, vp]
+        lib.attn_merge.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i, vp, vp, i, i, i, i, vp]
+        lib.attn_bwd_block_workspace_bytes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(sz)]
+        lib.attn_bwd_block_begin.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, i, i, vp]
+        lib.attn_bwd_block_dq.argtypes = [vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, ll, ll, f, vp]
+        lib.attn_bwd_block_dq_end.argtypes = [vp, vp, sz, i, i, i, i, i, i, f, vp]
+        lib.attn_bwd_block_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, ll, ll, f, vp]
+        for name in ("attn_fwd_block", "attn_merge", "attn_bwd_block_workspace_bytes", "attn_bwd_block_begin",
+                     "attn_bwd_block_dq", "attn_bwd_block_dq_end", "attn_bwd_block_dkdv"):
+            getattr(lib, name).restype = i
         _lib = lib
         return lib
 
@@ -196,3 +209,103 @@ def backward(q, k, v, o, dout, lse, causal=True, scale=None, stream=None, worksp
     ws = workspace_for(q, k) if workspace is None else workspace
     attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, causal, scale, stream)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# context-parallel building block (include/attn_block.h)
+# ---------------------------------------------------------------------------
+def _block_shape(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q shape {tuple(q.shape)}")
+    return B, Hq, k.shape[1], Sq, k.shape[2], D
+
+
+def _ws_ptr(workspace):
+    import torch
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    return workspace.data_ptr(), workspace.numel()
+
+
+def _raise(st, what):
+    if st != 0:
+        raise AttnError(st, what)
+
+
+def attn_fwd_block(q, k, v, o_part, lse_part, q_pos0, k_pos0, causal=True, scale=None, stream=None) -> None:
+    """Partial output (fp32) and log-sum-exp of one (query block, key block) pair."""
+    import torch
+    B, Hq, Hkv, Sq, Sk, D = _block_shape(q, k)
+    bf, f32 = torch.bfloat16, torch.float32
+    p = [_check(q, "q", bf, (B, Hq, Sq, D)), _check(k, "k", bf, (B, Hkv, Sk, D)),
+         _check(v, "v", bf, (B, Hkv, Sk, D)), _check(o_part, "o_part", f32, (B, Hq, Sq, D)),
+         _check(lse_part, "lse_part", f32, (B, Hq, Sq))]
+    _raise(load().attn_fwd_block(*p, B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), int(q_pos0), int(k_pos0),
+                                 _scale(scale, D), _stream(stream)), "attn_fwd_block")
+
+
+def attn_merge(o_parts, lse_parts, o, lse, stream=None) -> None:
+    """Merge partial results over disjoint key blocks into o (bf16) and lse."""
+    import torch
+    n = len(o_parts)
+    if n != len(lse_parts):
+        raise ValueError("o_parts and lse_parts differ in length")
+    B, Hq, Sq, D = o.shape
+    op = [_check(t, "o_parts[i]", torch.float32, (B, Hq, Sq, D)) for t in o_parts]
+    lp = [_check(t, "lse_parts[i]", torch.float32, (B, Hq, Sq)) for t in lse_parts]
+    arr = ctypes.c_void_p * max(n, 1)
+    _raise(load().attn_merge(arr(*op), arr(*lp), n, _check(o, "o", torch.bfloat16, (B, Hq, Sq, D)),
+                             _check(lse, "lse", torch.float32, (B, Hq, Sq)), B, Hq, Sq, D, _stream(stream)),
+           "attn_merge")
+
+
+def attn_bwd_block_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, D: int) -> int:
+    out = ctypes.c_size_t(0)
+    _raise(load().attn_bwd_block_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, ctypes.byref(out)),
+           "attn_bwd_block_workspace_bytes")
+    return out.value
+
+
+def attn_bwd_block_begin(o, dout, lse, workspace, Hkv, Sk, stream=None) -> None:
+    import torch
+    B, Hq, Sq, D = o.shape
+    bf = torch.bfloat16
+    p = [_check(o, "o", bf, (B, Hq, Sq, D)), _check(dout, "dout", bf, (B, Hq, Sq, D)),
+         _check(lse, "lse", torch.float32, (B, Hq, Sq))]
+    _raise(load().attn_bwd_block_begin(*p, *_ws_ptr(workspace), B, Hq, Hkv, Sq, Sk, D, _stream(stream)),
+           "attn_bwd_block_begin")
+
+
+def attn_bwd_block_dq(q, k, v, dout, workspace, q_pos0, k_pos0, causal=True, scale=None, stream=None) -> None:
+    import torch
+    B, Hq, Hkv, Sq, Sk, D = _block_shape(q, k)
+    bf = torch.bfloat16
+    p = [_check(q, "q", bf, (B, Hq, Sq, D)), _check(k, "k", bf, (B, Hkv, Sk, D)),
+         _check(v, "v", bf, (B, Hkv, Sk, D)), _check(dout, "dout", bf, (B, Hq, Sq, D))]
+    _raise(load().attn_bwd_block_dq(*p, *_ws_ptr(workspace), B, Hq, Hkv, Sq, Sk, D, int(bool(causal)),
+                                    int(q_pos0), int(k_pos0), _scale(scale, D), _stream(stream)),
+           "attn_bwd_block_dq")
+
+
+def attn_bwd_block_dq_end(dq, workspace, Hkv, Sk, scale=None, stream=None) -> None:
+    import torch
+    B, Hq, Sq, D = dq.shape
+    _raise(load().attn_bwd_block_dq_end(_check(dq, "dq", torch.bfloat16, (B, Hq, Sq, D)), *_ws_ptr(workspace),
+                                        B, Hq, Hkv, Sq, Sk, D, _scale(scale, D), _stream(stream)),
+           "attn_bwd_block_dq_end")
+
+
+def attn_bwd_block_dkdv(q, k, v, dout, dk, dv, workspace, q_pos0, k_pos0, causal=True, scale=None,
+                        stream=None) -> None:
+    import torch
+    B, Hq, Hkv, Sq, Sk, D = _block_shape(q, k)
+    bf = torch.bfloat16
+    p = [_check(q, "q", bf, (B, Hq, Sq, D)), _check(k, "k", bf, (B, Hkv, Sk, D)),
+         _check(v, "v", bf, (B, Hkv, Sk, D)), _check(dout, "dout", bf, (B, Hq, Sq, D)),
+         _check(dk, "dk", bf, (B, Hkv, Sk, D)), _check(dv, "dv", bf, (B, Hkv, Sk, D))]
+    _raise(load().attn_bwd_block_dkdv(*p, *_ws_ptr(workspace), B, Hq, Hkv, Sq, Sk, D, int(bool(causal)),
+                                      int(q_pos0), int(k_pos0), _scale(scale, D), _stream(stream)),
+           "attn_bwd_block_dkdv")

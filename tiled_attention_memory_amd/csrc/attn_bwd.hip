@@ -56,7 +56,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int choose_head_split(const AttnShape& sh) {
   const int g = sh.Hq / sh.Hkv;
-  const long long units = (long long)sh.B * sh.Hkv * ((sh.S + kKBC - 1) / kKBC);
+  const long long units = (long long)sh.B * sh.Hkv * ((sh.Sk + kKBC - 1) / kKBC);
   int ns = 1;
   while (units * ns < kTargetUnits && ns < g) {
     int next = ns + 1;
@@ -67,18 +67,29 @@ int choose_head_split(const AttnShape& sh) {
 }
 
 struct WsLayout {
-  size_t delta, lse2, part, total;
+  size_t delta, lse2, csum, acc_dq, acc_pk, part, total;
   int nsplit;
 };
 
-WsLayout ws_layout(const AttnShape& sh) {
+// Backward workspace. Whole-sequence pass: Delta, lse2 and the dK/dV partials.
+// Block protocol (block = true): also the running c = sum dS~ per row and the
+// fp32 sums of dS~ K and P K over the key blocks seen so far.
+WsLayout ws_layout(const AttnShape& sh, bool block = false) {
   WsLayout w;
-  const size_t rows = (size_t)sh.B * sh.Hq * sh.S;
+  const size_t rows = (size_t)sh.B * sh.Hq * sh.Sq;
   w.nsplit = choose_head_split(sh);
   w.delta = 0;
   w.lse2 = align256(rows * 4);
-  w.part = w.lse2 + align256(rows * 4);
-  const size_t kv_elems = (size_t)sh.B * sh.Hkv * sh.S * sh.D;
+  size_t off = w.lse2 + align256(rows * 4);
+  w.csum = w.acc_dq = w.acc_pk = 0;
+  if (block) {
+    w.csum = off;
+    w.acc_dq = w.csum + align256(rows * 4);
+    w.acc_pk = w.acc_dq + align256(rows * sh.D * 4);
+    off = w.acc_pk + align256(rows * sh.D * 4);
+  }
+  w.part = off;
+  const size_t kv_elems = (size_t)sh.B * sh.Hkv * sh.Sk * sh.D;
   w.total = w.part + (w.nsplit > 1 ? align256((size_t)w.nsplit * 2 * kv_elems * 4) : 0);
   return w;
 }
@@ -108,7 +119,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(const uint16_t*
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && part == 0) {
     delta[row] = acc;
-    lse2[row] = lse[row] * kLog2e;
+    // a row that sees no key at all has LSE = -inf; +inf here makes every
+    // recomputed probability of that row exactly 0
+    lse2[row] = lse[row] == -INFINITY ? INFINITY : lse[row] * kLog2e;
   }
 }
 
@@ -124,8 +137,8 @@ struct DkdvArgs {
   const float* lse2;
   uint16_t* dk;
   uint16_t* dv;
-  float* part;  // [nsplit][2][B*Hkv*S*D] fp32 partials when nsplit > 1
-  int Hq, Hkv, S, nsplit;
+  float* part;  // [nsplit][2][B*Hkv*Sk*D] fp32 partials when nsplit > 1
+  int Hq, Hkv, Sq, Sk, dlt, nsplit;
   float c;      // scale * log2(e)
   float scale;
   TileSched sched;  // streams = (batch*Hkv + kv head) * nsplit + subset; tiles = key tiles
@@ -171,8 +184,8 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   const int kblk = wave & 3;         // this wave's 32 keys within the unit
   const bool vrole = wave < 4;       // P and dV (with K resident); else dP, dS and dK (with V resident)
   const int col = lane & 31, half = lane >> 5;
-  const int S = a.S;
-  const size_t kv_base = (size_t)grp * S * D;
+  const int Sq = a.Sq, Sk = a.Sk, dlt = a.dlt;
+  const size_t kv_base = (size_t)grp * Sk * D;
   const int kvt0 = jt * kKBC;
   const int kvb0 = kvt0 + 32 * kblk;   // this wave's first key
   const int kvrow = kvb0 + col;        // the key this lane owns
@@ -184,7 +197,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
     const uint16_t* src = (vrole ? a.k : a.v) + kv_base + (size_t)kvrow * D + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kvf[ks] = kvrow < S ? *reinterpret_cast<const bf16x8*>(src + 16 * ks)
+      kvf[ks] = kvrow < Sk ? *reinterpret_cast<const bf16x8*>(src + 16 * ks)
                           : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
 
@@ -202,9 +215,10 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   // this lane's slots of the P hand-off block: element v of 32-row block qs at (16 qs + v) * 64 + lane
   float* pbuf = reinterpret_cast<float*>(smem + L::PB + kblk * L::PB_BLOCK) + lane;
 
-  const int NQ = (S + kKBR - 1) / kKBR;
-  const int i_min = CAUSAL ? kvt0 / kKBR : 0;
-  const int per_head = NQ - i_min;       // query tiles visited per head
+  const int NQ = (Sq + kKBR - 1) / kKBR;
+  // first query tile with a row that sees the unit's first key (row >= kvt0 - dlt)
+  const int i_min = CAUSAL ? (kvt0 - dlt <= 0 ? 0 : (kvt0 - dlt) / kKBR) : 0;
+  const int per_head = max(0, NQ - i_min);  // query tiles visited per head
   const int nsteps = per_head * hps;
 
   // step -> (query head, query tile): tiles run from the last one down, the
@@ -218,13 +232,13 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 #pragma unroll
   for (int i = 0; i < SLD; ++i) sld[i] = T::load_src((wave * SLD + i) % T::LOADS, lane);
 
-  // Q, dO tiles and their lse2, delta rows straight into stage `stg`; rows past S read as zeros.
+  // Q, dO tiles and their lse2, delta rows straight into stage `stg`; rows past Sq read as zeros.
   auto issue = [&](int st, int stg) TAM_INLINE {
     const int hq = step_head(st), row0 = step_tile(st) * kKBR;
     const size_t bh = (size_t)b * a.Hq + hq;
-    const int rows_left = S - row0;
-    const __amdgpu_buffer_rsrc_t rqd = make_rsrc(a.q + (bh * S + row0) * D, rows_left * D * 2);
-    const __amdgpu_buffer_rsrc_t rdd = make_rsrc(a.dout + (bh * S + row0) * D, rows_left * D * 2);
+    const int rows_left = Sq - row0;
+    const __amdgpu_buffer_rsrc_t rqd = make_rsrc(a.q + (bh * Sq + row0) * D, rows_left * D * 2);
+    const __amdgpu_buffer_rsrc_t rdd = make_rsrc(a.dout + (bh * Sq + row0) * D, rows_left * D * 2);
     const uint32_t base = lds0 + (stg ? L::Q1 : L::Q0);
 #pragma unroll
     for (int i = 0; i < SLD; ++i) {
@@ -233,7 +247,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
     }
     if (wave < 2) {
       const float* src = wave == 0 ? a.lse2 : a.delta;
-      const __amdgpu_buffer_rsrc_t rf = make_rsrc(src + bh * S + row0, rows_left * 4);
+      const __amdgpu_buffer_rsrc_t rf = make_rsrc(src + bh * Sq + row0, rows_left * 4);
       dma4(rf, lds0 + (stg ? L::F1 : L::F0) + wave * kKBR * 4, lane * 4);
     }
   };
@@ -256,7 +270,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
     const float* Fs = reinterpret_cast<const float*>(smem + FB);
     bool run[2];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) run[qs] = !(MASKED && CAUSAL && it * kKBR + qs * 32 + 31 < kvb0);
+    for (int qs = 0; qs < 2; ++qs) run[qs] = !(MASKED && CAUSAL && it * kKBR + qs * 32 + 31 + dlt < kvb0);
     // Products over the head dim: S = Q K^T (P role) or dP = dO V^T (dS role);
     // lane holds key kvrow, rows it*64 + 32qs + 8(v/4) + 4half + v%4.
     const int AB = vrole ? QB : DOB;
@@ -284,7 +298,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
             float e = fast_exp2(fmaf(x[qs][v], c, -l2[r]));
             if (MASKED) {
               const int qrow = it * kKBR + qs * 32 + 8 * i + 4 * half + r;
-              const bool ok = run[qs] && qrow < S && kvrow < S && (!CAUSAL || kvrow <= qrow);
+              const bool ok = run[qs] && qrow < Sq && kvrow < Sk && (!CAUSAL || kvrow <= qrow + dlt);
               e = ok ? e : 0.f;
             }
             p[v] = e;
@@ -338,7 +352,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
     const int it = step_tile(st);
     // the whole workgroup takes the same branch: the tile meets the diagonal of
     // the unit's 128 keys, or the end of the sequence
-    const bool masked = (CAUSAL && it * kKBR < kvt0 + kKBC) || it * kKBR + kKBR > S || kvt0 + kKBC > S;
+    const bool masked = (CAUSAL && it * kKBR + dlt < kvt0 + kKBC) || it * kKBR + kKBR > Sq || kvt0 + kKBC > Sk;
     if (masked)
       tile(std::true_type{}, stage_tag, it);
     else
@@ -356,7 +370,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   }
 
   // lane holds key kvrow, head-dim entries 32db + 8i + 4half + (0..3)
-  if (kvrow < S) {
+  if (kvrow < Sk) {
     const float mul = vrole ? 1.f : a.scale;
     if (a.nsplit == 1) {
       uint16_t* op = (vrole ? a.dv : a.dk) + kv_base + (size_t)kvrow * D + 8 * half;
@@ -374,7 +388,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
           *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
         }
     } else {
-      const size_t total = (size_t)(a.sched.BH / a.nsplit) * S * D;  // B*Hkv*S*D
+      const size_t total = (size_t)(a.sched.BH / a.nsplit) * Sk * D;  // B*Hkv*Sk*D
       float* op = a.part + ((size_t)sub * 2 + (vrole ? 1 : 0)) * total + kv_base + (size_t)kvrow * D + 4 * half;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -414,10 +428,16 @@ struct DqArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  float* delta;  // in: Delta~ from the stored O; out: exact Delta
+  float* delta;  // in: Delta~ from the stored O; out: exact Delta (final mode)
   const float* lse2;
-  uint16_t* dq;
-  int Hq, Hkv, S;
+  uint16_t* dq;  // final mode: dQ = scale (sum dS~ K - c P K)
+  // Accumulate mode (all three set, dq unused): this call's key block adds its
+  // sum dS~ K, P K and c = sum dS~ to these fp32 buffers ([rows, D], [rows, D],
+  // [rows]); the sum over all key blocks is finished later.
+  float* acc_dq;
+  float* acc_pk;
+  float* acc_c;
+  int Hq, Hkv, Sq, Sk, dlt;
   float c;
   float scale;
   TileSched sched;
@@ -454,12 +474,12 @@ void attn_bwd_dq_kernel(DqArgs a) {
   const int rblk = wave & 3;         // this pair's 32 query rows within the unit
   const bool prole = wave < 4;       // S, P and P K (with Q resident); else dP, dS and dQ (with dO resident)
   const int col = lane & 31, half = lane >> 5;
-  const int S = a.S;
+  const int Sq = a.Sq, Sk = a.Sk, dlt = a.dlt;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int kvh = h / (a.Hq / a.Hkv);
-  const size_t q_base = (size_t)bh * S * D;
-  const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
-  const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
+  const size_t q_base = (size_t)bh * Sq * D;
+  const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)Sk * D;
+  const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)Sk * D;
   const int q0 = qt * kQBR;
   const int wrow0 = q0 + rblk * 32;
   const int qrow = wrow0 + col;
@@ -471,10 +491,10 @@ void attn_bwd_dq_kernel(DqArgs a) {
     const uint16_t* src = (prole ? a.q : a.dout) + q_base + (size_t)qrow * D + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      xf[ks] = qrow < S ? *reinterpret_cast<const bf16x8*>(src + 16 * ks)
+      xf[ks] = qrow < Sq ? *reinterpret_cast<const bf16x8*>(src + 16 * ks)
                         : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
-  const float rowval = qrow < S ? (prole ? a.lse2 : a.delta)[(size_t)bh * S + qrow] : 0.f;  // lse2 or Delta~
+  const float rowval = qrow < Sq ? (prole ? a.lse2 : a.delta)[(size_t)bh * Sq + qrow] : 0.f;  // lse2 or Delta~
 
   // per-lane LDS offsets, fixed for every tile (see SwzTile)
   const int i16 = lane & 15;
@@ -492,14 +512,15 @@ void attn_bwd_dq_kernel(DqArgs a) {
   // this lane's slots of the P hand-off block: key v of 32-key block kb at (16 kb + v) * 64 + lane
   float* pbuf = reinterpret_cast<float*>(smem + L::PB + rblk * L::PB_BLOCK) + lane;
 
-  const int last_row = min(q0 + kQBR, S) - 1;
-  const int n_kv = (S + kQBC - 1) / kQBC;
-  const int ntiles = CAUSAL ? min(n_kv, last_row / kQBC + 1) : n_kv;
+  const int last_row = min(q0 + kQBR, Sq) - 1;
+  const int n_kv = (Sk + kQBC - 1) / kQBC;
+  // the last key any row of the unit may see is last_row + dlt
+  const int ntiles = CAUSAL ? (last_row + dlt < 0 ? 0 : min(n_kv, (last_row + dlt) / kQBC + 1)) : n_kv;
 
-  // K and V tiles straight into stage `stg`; rows past S read as zeros.
+  // K and V tiles straight into stage `stg`; rows past Sk read as zeros.
   auto issue = [&](int j, int stg) TAM_INLINE {
     const int row0 = j * kQBC;
-    const int bytes = (S - row0) * D * 2;
+    const int bytes = (Sk - row0) * D * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)row0 * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)row0 * D, bytes);
     const uint32_t base = lds0 + (stg ? L::K1 : L::K0);
@@ -556,7 +577,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
           float e = fast_exp2(fmaf(x[kb][v], c, -rowval));
           if (MASKED) {
             const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-            const bool ok = kv < S && (!CAUSAL || kv <= qrow);
+            const bool ok = kv < Sk && (!CAUSAL || kv <= qrow + dlt);
             e = ok ? e : 0.f;
           }
           pf[v] = e;
@@ -615,10 +636,10 @@ void attn_bwd_dq_kernel(DqArgs a) {
     constexpr int STG = decltype(stage_tag)::value;
     if (j + 1 < ntiles) issue(j + 1, STG ^ 1);
     const int kv0 = j * kQBC;
-    const bool active = !CAUSAL || kv0 <= wrow0 + 31;
+    const bool active = !CAUSAL || kv0 <= wrow0 + 31 + dlt;
     if (prole) {
       // uniform per wave: the tile meets the pair's diagonal or the end of the sequence
-      const bool masked = (kv0 + kQBC > S) || (CAUSAL && kv0 + kQBC - 1 > wrow0);
+      const bool masked = (kv0 + kQBC > Sk) || (CAUSAL && kv0 + kQBC - 1 > wrow0 + dlt);
       if (masked)
         tile_p(std::true_type{}, stage_tag, kv0, active);
       else
@@ -630,7 +651,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
     __syncthreads();
   };
 
-  issue(0, 0);
+  if (ntiles > 0) issue(0, 0);
   wait_loads();
   __syncthreads();
   for (int j = 0; j < ntiles; j += 2) {
@@ -638,6 +659,24 @@ void attn_bwd_dq_kernel(DqArgs a) {
     if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
+  if (a.acc_dq) {
+    // accumulate mode: each role adds its own sums for this key block
+    if (qrow < Sq && ntiles > 0) {
+      float* dst = (prole ? a.acc_pk : a.acc_dq) + q_base + (size_t)qrow * D + 4 * half;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4* p4 = reinterpret_cast<f32x4*>(dst + 32 * db + 8 * i);
+          *p4 += f32x4{acc[db][4 * i], acc[db][4 * i + 1], acc[db][4 * i + 2], acc[db][4 * i + 3]};
+        }
+      if (!prole) {
+        const float cs = sum_halves(csum);
+        if (half == 0) a.acc_c[(size_t)bh * Sq + qrow] += cs;
+      }
+    }
+    return;
+  }
   // P K goes to the dS role through the (now idle) stages: element v of
   // accumulator db of lane l at float (16 db + v) * 64 + l of the pair's block.
   float* hand = reinterpret_cast<float*>(smem) + rblk * (DB * 16 * 64) + lane;
@@ -650,7 +689,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
   __syncthreads();
   if (prole) return;
   const float corr = sum_halves(csum);  // Delta_i - Delta~_i
-  if (qrow < S) {
+  if (qrow < Sq) {
     uint16_t* op = a.dq + q_base + (size_t)qrow * D + 8 * half;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -668,107 +707,250 @@ void attn_bwd_dq_kernel(DqArgs a) {
         }
         *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
       }
-    if (half == 0) a.delta[(size_t)bh * S + qrow] = rowval + corr;
+    if (half == 0) a.delta[(size_t)bh * Sq + qrow] = rowval + corr;
   }
 }
 
 // ---------------------------------------------------------------------------
+// 5. small kernels of the block protocol
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void attn_fill_zero_kernel(f32x4* p, long long n4) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n4) p[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// dQ = scale (sum dS~ K - c P K) in bf16, and the exact Delta = Delta~ + c.
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_dq_end_kernel(const float* acc_dq, const float* acc_pk,
+                                                                   const float* csum, float* delta,
+                                                                   uint16_t* dq, float scale, long long rows) {
+  constexpr int TPR = D / 8;  // threads per row, 8 elements each
+  constexpr int RPB = kThreads / TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  if (row >= rows) return;
+  const float c = csum[row];
+  const f32x4* a = reinterpret_cast<const f32x4*>(acc_dq + row * D + part * 8);
+  const f32x4* p = reinterpret_cast<const f32x4*>(acc_pk + row * D + part * 8);
+  u32x4 w;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x4 x = a[h], y = p[h];
+    w[2 * h] = pack_bf16(scale * fmaf(-c, y[0], x[0]), scale * fmaf(-c, y[1], x[1]));
+    w[2 * h + 1] = pack_bf16(scale * fmaf(-c, y[2], x[2]), scale * fmaf(-c, y[3], x[3]));
+  }
+  *reinterpret_cast<u32x4*>(dq + row * D + part * 8) = w;
+  if (part == 0) delta[row] += c;
+}
+
+// ---------------------------------------------------------------------------
+// host side: one launcher per stage, shared by the whole-sequence pass and
+// the block protocol
+// ---------------------------------------------------------------------------
+struct Ws {
+  float *delta, *lse2, *csum, *acc_dq, *acc_pk, *part;
+  WsLayout w;
+  Ws(const AttnShape& sh, void* base, bool block) : w(ws_layout(sh, block)) {
+    char* b = static_cast<char*>(base);
+    delta = reinterpret_cast<float*>(b + w.delta);
+    lse2 = reinterpret_cast<float*>(b + w.lse2);
+    csum = block ? reinterpret_cast<float*>(b + w.csum) : nullptr;
+    acc_dq = block ? reinterpret_cast<float*>(b + w.acc_dq) : nullptr;
+    acc_pk = block ? reinterpret_cast<float*>(b + w.acc_pk) : nullptr;
+    part = reinterpret_cast<float*>(b + w.part);
+  }
+};
+
+template <int D>
+hipError_t launch_prep(const AttnShape& sh, const uint16_t* o, const uint16_t* dout, const float* lse,
+                       const Ws& ws, hipStream_t stream) {
+  const long long rows = (long long)sh.B * sh.Hq * sh.Sq;
+  constexpr int RPB = kThreads / (D / 8);
+  const long long grid = (rows + RPB - 1) / RPB;
+  float* delta = ws.delta;
+  float* lse2 = ws.lse2;
+  void* args[] = {(void*)&o, (void*)&dout, (void*)&lse, (void*)&delta, (void*)&lse2, (void*)&rows};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_prep_kernel<D>), dim3((unsigned)grid),
+                         dim3(kThreads), args, 0, stream);
+}
+
+// Zero n floats (n a multiple of 4) with a kernel, so the protocol stays
+// capturable in a graph.
+hipError_t launch_fill_zero(float* p, long long n, hipStream_t stream) {
+  long long n4 = n / 4;
+  const long long grid = (n4 + kThreads - 1) / kThreads;
+  f32x4* p4 = reinterpret_cast<f32x4*>(p);
+  void* args[] = {(void*)&p4, (void*)&n4};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fill_zero_kernel), dim3((unsigned)grid),
+                         dim3(kThreads), args, 0, stream);
+}
+
+// dQ kernel: final mode (dq set) or accumulate mode (dq null).
+template <int D, bool CAUSAL>
+hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     const uint16_t* dout, uint16_t* dq, const Ws& ws, hipStream_t stream) {
+  DqArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.delta = ws.delta;
+  a.lse2 = ws.lse2;
+  a.dq = dq;
+  a.acc_dq = dq ? nullptr : ws.acc_dq;
+  a.acc_pk = dq ? nullptr : ws.acc_pk;
+  a.acc_c = dq ? nullptr : ws.csum;
+  a.Hq = sh.Hq;
+  a.Hkv = sh.Hkv;
+  a.Sq = sh.Sq;
+  a.Sk = sh.Sk;
+  a.dlt = sh.dlt;
+  a.c = sh.scale * kLog2e;
+  a.scale = sh.scale;
+  a.sched.BH = sh.B * sh.Hq;
+  a.sched.NT = (sh.Sq + kQBR - 1) / kQBR;
+  a.sched.chunk = (a.sched.BH + 7) / 8;
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL>),
+                         dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const uint16_t* dout, uint16_t* dk, uint16_t* dv, const Ws& ws, hipStream_t stream) {
+  DkdvArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.delta = ws.delta;
+  a.lse2 = ws.lse2;
+  a.dk = dk;
+  a.dv = dv;
+  a.part = ws.part;
+  a.Hq = sh.Hq;
+  a.Hkv = sh.Hkv;
+  a.Sq = sh.Sq;
+  a.Sk = sh.Sk;
+  a.dlt = sh.dlt;
+  a.nsplit = ws.w.nsplit;
+  a.c = sh.scale * kLog2e;
+  a.scale = sh.scale;
+  a.sched.BH = sh.B * sh.Hkv * ws.w.nsplit;
+  a.sched.NT = (sh.Sk + kKBC - 1) / kKBC;
+  a.sched.chunk = (a.sched.BH + 7) / 8;
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL>),
+                         dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
+}
+
+hipError_t launch_reduce(const AttnShape& sh, uint16_t* dk, uint16_t* dv, const Ws& ws, hipStream_t stream) {
+  if (ws.w.nsplit <= 1) return hipSuccess;
+  const long long n4 = (long long)sh.B * sh.Hkv * sh.Sk * sh.D / 4;
+  const long long grid = (n4 + kThreads - 1) / kThreads;
+  int ns = ws.w.nsplit;
+  float* part = ws.part;
+  void* args[] = {(void*)&part, (void*)&dk, (void*)&dv, (void*)&n4, (void*)&ns};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_reduce_kernel), dim3((unsigned)grid),
+                         dim3(kThreads), args, 0, stream);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_all(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* o, const uint16_t* dout, const float* lse, uint16_t* dq,
                       uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t stream,
                       hipEvent_t* ev) {
-  const WsLayout w = ws_layout(sh);
-  char* ws = static_cast<char*>(workspace);
-  float* delta = reinterpret_cast<float*>(ws + w.delta);
-  float* lse2 = reinterpret_cast<float*>(ws + w.lse2);
-  float* part = reinterpret_cast<float*>(ws + w.part);
-  const float c = sh.scale * kLog2e;
+  const Ws ws(sh, workspace, false);
   hipError_t e;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return e;
-
-  {  // 1. prep
-    const long long rows = (long long)sh.B * sh.Hq * sh.S;
-    constexpr int RPB = kThreads / (D / 8);
-    const long long grid = (rows + RPB - 1) / RPB;
-    void* args[] = {(void*)&o, (void*)&dout, (void*)&lse, (void*)&delta, (void*)&lse2, (void*)&rows};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_prep_kernel<D>), dim3((unsigned)grid),
-                        dim3(kThreads), args, 0, stream);
-    if (e != hipSuccess || (e = mark(1)) != hipSuccess) return e;
-  }
-  {  // 2. dQ (also turns Delta~ into the exact Delta)
-    DqArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.dout = dout;
-    a.delta = delta;
-    a.lse2 = lse2;
-    a.dq = dq;
-    a.Hq = sh.Hq;
-    a.Hkv = sh.Hkv;
-    a.S = sh.S;
-    a.c = c;
-    a.scale = sh.scale;
-    a.sched.BH = sh.B * sh.Hq;
-    a.sched.NT = (sh.S + kQBR - 1) / kQBR;
-    a.sched.chunk = (a.sched.BH + 7) / 8;
-    void* args[] = {&a};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL>),
-                        dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
-    if (e != hipSuccess || (e = mark(2)) != hipSuccess) return e;
-  }
-  {  // 3. dK/dV
-    DkdvArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.dout = dout;
-    a.delta = delta;
-    a.lse2 = lse2;
-    a.dk = dk;
-    a.dv = dv;
-    a.part = part;
-    a.Hq = sh.Hq;
-    a.Hkv = sh.Hkv;
-    a.S = sh.S;
-    a.nsplit = w.nsplit;
-    a.c = c;
-    a.scale = sh.scale;
-    a.sched.BH = sh.B * sh.Hkv * w.nsplit;
-    a.sched.NT = (sh.S + kKBC - 1) / kKBC;
-    a.sched.chunk = (a.sched.BH + 7) / 8;
-    void* args[] = {&a};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL>),
-                        dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
-    if (e != hipSuccess || (e = mark(3)) != hipSuccess) return e;
-  }
-  if (w.nsplit > 1) {  // 4. fixed-order sum of the head-subset partials
-    const long long n4 = (long long)sh.B * sh.Hkv * sh.S * sh.D / 4;
-    const long long grid = (n4 + kThreads - 1) / kThreads;
-    int ns = w.nsplit;
-    void* args[] = {(void*)&part, (void*)&dk, (void*)&dv, (void*)&n4, (void*)&ns};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_reduce_kernel), dim3((unsigned)grid),
-                        dim3(kThreads), args, 0, stream);
-    if (e != hipSuccess) return e;
-  }
+  // 1. Delta~ and lse2
+  if ((e = launch_prep<D>(sh, o, dout, lse, ws, stream)) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
+  // 2. dQ (also turns Delta~ into the exact Delta)
+  if ((e = launch_dq<D, CAUSAL>(sh, q, k, v, dout, dq, ws, stream)) != hipSuccess || (e = mark(2)) != hipSuccess)
+    return e;
+  // 3. dK/dV
+  if ((e = launch_dkdv<D, CAUSAL>(sh, q, k, v, dout, dk, dv, ws, stream)) != hipSuccess ||
+      (e = mark(3)) != hipSuccess)
+    return e;
+  // 4. fixed-order sum of the head-subset partials
+  if ((e = launch_reduce(sh, dk, dv, ws, stream)) != hipSuccess) return e;
   return mark(4);
+}
+
+template <int D>
+hipError_t block_begin(const AttnShape& sh, const uint16_t* o, const uint16_t* dout, const float* lse,
+                       void* workspace, hipStream_t stream) {
+  const Ws ws(sh, workspace, true);
+  hipError_t e = launch_prep<D>(sh, o, dout, lse, ws, stream);
+  // the three accumulators are contiguous: c [rows] then the two [rows, D]
+  // sums, each padded to 256 bytes
+  if (e == hipSuccess) e = launch_fill_zero(ws.csum, (long long)((ws.w.part - ws.w.csum) / 4), stream);
+  return e;
+}
+
+template <int D>
+hipError_t block_dq_end(const AttnShape& sh, uint16_t* dq, void* workspace, hipStream_t stream) {
+  const Ws ws(sh, workspace, true);
+  const long long rows = (long long)sh.B * sh.Hq * sh.Sq;
+  constexpr int RPB = kThreads / (D / 8);
+  const long long grid = (rows + RPB - 1) / RPB;
+  const float* acc_dq = ws.acc_dq;
+  const float* acc_pk = ws.acc_pk;
+  const float* csum = ws.csum;
+  float* delta = ws.delta;
+  float scale = sh.scale;
+  void* args[] = {(void*)&acc_dq, (void*)&acc_pk, (void*)&csum, (void*)&delta, (void*)&dq, (void*)&scale,
+                  (void*)&rows};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_end_kernel<D>), dim3((unsigned)grid),
+                         dim3(kThreads), args, 0, stream);
+}
+
+template <int D, bool CAUSAL>
+hipError_t block_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* dout, uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t stream) {
+  const Ws ws(sh, workspace, true);
+  hipError_t e = launch_dkdv<D, CAUSAL>(sh, q, k, v, dout, dk, dv, ws, stream);
+  if (e != hipSuccess) return e;
+  return launch_reduce(sh, dk, dv, ws, stream);
 }
 
 }  // namespace
 
 size_t bwd_workspace_bytes(const AttnShape& sh) { return ws_layout(sh).total; }
+size_t bwd_block_workspace_bytes(const AttnShape& sh) { return ws_layout(sh, true).total; }
+
+#define TAM_DISPATCH(F, ...)                                                              \
+  (sh.D == 128 ? (sh.causal ? F<128, true>(__VA_ARGS__) : F<128, false>(__VA_ARGS__))   \
+               : (sh.causal ? F<64, true>(__VA_ARGS__) : F<64, false>(__VA_ARGS__)))
 
 hipError_t launch_bwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* o, const uint16_t* dout, const float* lse, uint16_t* dq,
                       uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t stream,
                       hipEvent_t* ev) {
-  if (sh.D == 128)
-    return sh.causal ? launch_all<128, true>(sh, q, k, v, o, dout, lse, dq, dk, dv, workspace, stream, ev)
-                     : launch_all<128, false>(sh, q, k, v, o, dout, lse, dq, dk, dv, workspace, stream, ev);
-  return sh.causal ? launch_all<64, true>(sh, q, k, v, o, dout, lse, dq, dk, dv, workspace, stream, ev)
-                   : launch_all<64, false>(sh, q, k, v, o, dout, lse, dq, dk, dv, workspace, stream, ev);
+  return TAM_DISPATCH(launch_all, sh, q, k, v, o, dout, lse, dq, dk, dv, workspace, stream, ev);
+}
+
+hipError_t launch_bwd_block_begin(const AttnShape& sh, const uint16_t* o, const uint16_t* dout, const float* lse,
+                                  void* workspace, hipStream_t stream) {
+  return sh.D == 128 ? block_begin<128>(sh, o, dout, lse, workspace, stream)
+                     : block_begin<64>(sh, o, dout, lse, workspace, stream);
+}
+
+hipError_t launch_bwd_block_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const uint16_t* dout, void* workspace, hipStream_t stream) {
+  const Ws ws(sh, workspace, true);
+  return TAM_DISPATCH(launch_dq, sh, q, k, v, dout, nullptr, ws, stream);
+}
+
+hipError_t launch_bwd_block_dq_end(const AttnShape& sh, uint16_t* dq, void* workspace, hipStream_t stream) {
+  return sh.D == 128 ? block_dq_end<128>(sh, dq, workspace, stream) : block_dq_end<64>(sh, dq, workspace, stream);
+}
+
+hipError_t launch_bwd_block_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const uint16_t* dout, uint16_t* dk, uint16_t* dv, void* workspace,
+                                 hipStream_t stream) {
+  return TAM_DISPATCH(block_dkdv, sh, q, k, v, dout, dk, dv, workspace, stream);
 }
 
 }  // namespace tam

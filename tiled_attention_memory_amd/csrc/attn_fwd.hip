@@ -6,6 +6,12 @@
 // products so that only O and one log-sum-exp per row are written to HBM
 // ("Kernel Fusion").
 //
+// The same kernel serves a block pair of context-parallel attention: Sq query
+// rows against Sk keys, key j visible to query row i when j <= i + dlt under a
+// causal mask (dlt = query position - key position of the blocks' first rows).
+// A row that sees no key gets O = 0 and LSE = -inf. With Sq = Sk and dlt = 0
+// this is plain causal attention.
+//
 // Work unit: one (batch, query head, 128-row query tile); 4 waves, each owning
 // 32 query rows. Per 64-key tile:
 //   S^T = K Q^T       (MFMA; A = K rows from LDS, B = Q rows held in registers)
@@ -36,9 +42,10 @@ struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  uint16_t* o;
+  uint16_t* o;      // bf16 output, or
+  float* o32;       // fp32 output (partial results of a block pair)
   float* lse;
-  int Hq, Hkv, S;
+  int Hq, Hkv, Sq, Sk, dlt;
   float c;  // softmax scale * log2(e): scores are exponentiated in base 2
   TileSched sched;
 };
@@ -68,12 +75,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
   const int col = lane & 31, half = lane >> 5;
-  const int S = a.S;
+  const int Sq = a.Sq, Sk = a.Sk, dlt = a.dlt;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int kvh = h / (a.Hq / a.Hkv);
-  const size_t q_base = (size_t)bh * S * D;
-  const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
-  const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)S * D;
+  const size_t q_base = (size_t)bh * Sq * D;
+  const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)Sk * D;
+  const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)Sk * D;
   const int q0 = qt * kBR;
   const int wrow0 = q0 + wave * 32;  // first query row of this wave
   const int qrow = wrow0 + col;      // the query row this lane owns
@@ -88,7 +95,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     const uint32_t flip = a.c < 0.f ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 w = qrow < S ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      u32x4 w = qrow < Sq ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
       w ^= flip;
       qf[ks] = __builtin_bit_cast(bf16x8, w);
     }
@@ -112,14 +119,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NLD; ++i) loff[i] = T::load_src(wave * NLD + i, lane);
 
-  const int last_row = min(q0 + kBR, S) - 1;
-  const int n_kv = (S + kBC - 1) / kBC;
-  const int ntiles = CAUSAL ? min(n_kv, last_row / kBC + 1) : n_kv;
+  const int last_row = min(q0 + kBR, Sq) - 1;
+  const int n_kv = (Sk + kBC - 1) / kBC;
+  // the last key any row of the unit may see is last_row + dlt
+  const int ntiles = CAUSAL ? (last_row + dlt < 0 ? 0 : min(n_kv, (last_row + dlt) / kBC + 1)) : n_kv;
 
   // K and V tile j straight into an LDS stage; rows past S read as zeros.
   auto issue = [&](int j, unsigned char* stage) TAM_INLINE {
     const int row0 = j * kBC;
-    const int bytes = (S - row0) * D * 2;
+    const int bytes = (Sk - row0) * D * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)row0 * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)row0 * D, bytes);
     unsigned char* dst = stage + wave * NLD * 1024;
@@ -162,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     // Whether this row may see the key of accumulator element v of block kb:
     // that key is kv0 + 32 KB0 + 4half + off with the constant
     // off = 32kb + 8(v/4) + v%4, so one compare against a per-lane limit decides it.
-    const int lim = (CAUSAL ? min(qrow, S - 1) : S - 1) - (kv0 + 32 * KB0 + 4 * half);
+    const int lim = (CAUSAL ? min(qrow + dlt, Sk - 1) : Sk - 1) - (kv0 + 32 * KB0 + 4 * half);
     auto visible = [&](int kb, int v) TAM_INLINE { return kb * 32 + 8 * (v >> 2) + (v & 3) <= lim; };
     if (MASKED) {
 #pragma unroll
@@ -183,8 +191,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     // The few masked tiles rescale unconditionally: a branch here would make
     // the compiler copy the accumulators and spill.
     if (MASKED || __builtin_amdgcn_ballot_w64(grow)) {
+      // 0 on a row's first visible tile, 1 where the max does not move (also
+      // for a row that has seen no key yet, where m_run - m_new would be NaN)
+      const float alpha = grow ? fast_exp2(m_run - mt) : 1.f;
       const float m_new = grow ? mt : m_run;
-      const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, 1 where unchanged
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -244,8 +254,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   // Leading tiles lie entirely below this wave's diagonal and inside the
   // sequence: they run unmasked, two per iteration with fixed stages. The
   // remaining few tiles (diagonal, ragged end) run one by one.
-  const int n_plain = min(ntiles, (CAUSAL ? min(wrow0 + 1, S) : S) / kBC);
-  issue(0, stage0);
+  const int n_plain = max(0, min(ntiles, (CAUSAL ? min(wrow0 + dlt + 1, Sk) : Sk) / kBC));
+  if (ntiles > 0) issue(0, stage0);
   wait_loads();
   __syncthreads();
   int j = 0;
@@ -264,13 +274,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
     using C2 = std::integral_constant<int, 2>;
-    if (!CAUSAL || kv0 <= wrow0 + 31) {   // some key of the tile is visible to this wave
+    if (!CAUSAL || kv0 <= wrow0 + 31 + dlt) {   // some key of the tile is visible to this wave
       if (jj < n_plain) {
         tile(std::false_type{}, C0{}, C2{}, kv0, cur);
       } else {
         tile(std::true_type{}, C0{}, C1{}, kv0, cur);
         // the second 32-key block, unless this wave sees none of its keys
-        if ((!CAUSAL || kv0 + 32 <= wrow0 + 31) && kv0 + 32 < S) tile(std::true_type{}, C1{}, C1{}, kv0, cur);
+        if ((!CAUSAL || kv0 + 32 <= wrow0 + 31 + dlt) && kv0 + 32 < Sk) tile(std::true_type{}, C1{}, C1{}, kv0, cur);
       }
     }
     wait_loads();
@@ -284,43 +294,58 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   }
 
   const float l_tot = sum_halves(l_run);
-  if (qrow < S) {
-    const float inv = 1.f / l_tot;
-    // lane holds columns 32db + 8i + 4half + (0..3); pairs of i are merged
-    // across the halves so each store writes 16 contiguous bytes per lane
-    uint16_t* op = a.o + q_base + (size_t)qrow * D + 8 * half;
+  if (qrow < Sq) {
+    // a row that saw no key (possible with offset blocks) gets O = 0, LSE = -inf
+    const bool seen = l_tot > 0.f;
+    const float inv = seen ? 1.f / l_tot : 0.f;
+    if (a.o32) {
+      float* op = a.o32 + q_base + (size_t)qrow * D + 4 * half;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        u32x2 w[2];
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<f32x4*>(op + 32 * db + 8 * i) =
+              f32x4{acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv, acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv};
+    } else {
+      // lane holds columns 32db + 8i + 4half + (0..3); pairs of i are merged
+      // across the halves so each store writes 16 contiguous bytes per lane
+      uint16_t* op = a.o + q_base + (size_t)qrow * D + 8 * half;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int i = 2 * m + t;
-          w[t] = u32x2{pack_bf16(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv),
-                       pack_bf16(acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv)};
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          u32x2 w[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int i = 2 * m + t;
+            w[t] = u32x2{pack_bf16(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv),
+                         pack_bf16(acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv)};
+          }
+          *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
         }
-        *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
-      }
-    if (half == 0) a.lse[(size_t)bh * S + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+    if (half == 0) a.lse[(size_t)bh * Sq + qrow] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                  uint16_t* o, float* lse, hipStream_t stream) {
+                  uint16_t* o, float* o32, float* lse, hipStream_t stream) {
   FwdArgs a;
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = o;
+  a.o32 = o32;
   a.lse = lse;
   a.Hq = sh.Hq;
   a.Hkv = sh.Hkv;
-  a.S = sh.S;
+  a.Sq = sh.Sq;
+  a.Sk = sh.Sk;
+  a.dlt = sh.dlt;
   a.c = sh.scale * kLog2e;
   a.sched.BH = sh.B * sh.Hq;
-  a.sched.NT = (sh.S + kBR - 1) / kBR;
+  a.sched.NT = (sh.Sq + kBR - 1) / kBR;
   a.sched.chunk = (a.sched.BH + 7) / 8;
   const long long grid = sched_grid(a.sched);
   void* args[] = {&a};
@@ -331,11 +356,11 @@ hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, con
 }  // namespace
 
 hipError_t launch_fwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                      uint16_t* o, float* lse, hipStream_t stream) {
-  if (sh.D == 128) return sh.causal ? launch<128, true>(sh, q, k, v, o, lse, stream)
-                                    : launch<128, false>(sh, q, k, v, o, lse, stream);
-  return sh.causal ? launch<64, true>(sh, q, k, v, o, lse, stream)
-                   : launch<64, false>(sh, q, k, v, o, lse, stream);
+                      uint16_t* o, float* o32, float* lse, hipStream_t stream) {
+  if (sh.D == 128) return sh.causal ? launch<128, true>(sh, q, k, v, o, o32, lse, stream)
+                                    : launch<128, false>(sh, q, k, v, o, o32, lse, stream);
+  return sh.causal ? launch<64, true>(sh, q, k, v, o, o32, lse, stream)
+                   : launch<64, false>(sh, q, k, v, o, o32, lse, stream);
 }
 
 }  // namespace tam

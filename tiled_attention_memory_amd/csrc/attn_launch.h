@@ -8,14 +8,25 @@
 
 namespace tam {
 
+// Sq query rows against Sk keys; under a causal mask key j is visible to
+// query row i when j <= i + dlt (dlt = query position - key position of the
+// first rows, clamped to [-Sq, Sk]). The whole-sequence calls use Sq = Sk and
+// dlt = 0.
 struct AttnShape {
-  int B, Hq, Hkv, S, D;
+  int B, Hq, Hkv, Sq, Sk, D;
   bool causal;
+  int dlt;
   float scale;
 };
 
+constexpr int kMaxMerge = 16;  // partial results one merge call combines
+
+// Exactly one of o (bf16) and o32 (fp32) is set.
 hipError_t launch_fwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                      uint16_t* o, float* lse, hipStream_t stream);
+                      uint16_t* o, float* o32, float* lse, hipStream_t stream);
+
+hipError_t launch_merge(const float* const* o_parts, const float* const* lse_parts, int n, uint16_t* o,
+                        float* lse, long long rows, int D, hipStream_t stream);
 
 // Workspace layout of the backward pass (bytes, 256-aligned offsets).
 size_t bwd_workspace_bytes(const AttnShape& sh);
@@ -24,5 +35,16 @@ hipError_t launch_bwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
                       const uint16_t* o, const uint16_t* dout, const float* lse, uint16_t* dq,
                       uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t stream,
                       hipEvent_t* events = nullptr);
+
+// Block protocol of the backward pass (one query block, key blocks in turn).
+size_t bwd_block_workspace_bytes(const AttnShape& sh);
+hipError_t launch_bwd_block_begin(const AttnShape& sh, const uint16_t* o, const uint16_t* dout, const float* lse,
+                                  void* workspace, hipStream_t stream);
+hipError_t launch_bwd_block_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const uint16_t* dout, void* workspace, hipStream_t stream);
+hipError_t launch_bwd_block_dq_end(const AttnShape& sh, uint16_t* dq, void* workspace, hipStream_t stream);
+hipError_t launch_bwd_block_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const uint16_t* dout, uint16_t* dk, uint16_t* dv, void* workspace,
+                                 hipStream_t stream);
 
 }  // namespace tam

@@ -1,0 +1,83 @@
+// Merge of partial attention results over disjoint key blocks, for gfx950.
+//
+// The page "使用 PyTorch FSDP 微調 Llama 2 70B" (agentlenshq.com), section
+// "Flash Attention", combines score tiles with an online softmax; a sequence
+// split across GPUs (context parallelism, run on the AMD MI300X pages at 32k
+// and 128k tokens) combines whole key blocks the same way. Each block b gives a
+// partial output O_b (normalised over its own keys) and its log-sum-exp LSE_b;
+// the result over all blocks is
+//   LSE = ln sum_b exp(LSE_b),   O = sum_b exp(LSE_b - LSE) O_b,
+// with parts whose LSE is -inf (rows that saw no key of that block) weighing 0
+// and a row that no block reaches left at O = 0, LSE = -inf.
+//
+// One pass over the rows, fp32 throughout, bf16 output: HBM-bound.
+#include <math.h>
+
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace tam {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct MergeArgs {
+  const float* o[kMaxMerge];
+  const float* lse[kMaxMerge];
+  int n;
+  uint16_t* out;
+  float* lse_out;
+  long long rows;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_merge_kernel(MergeArgs a) {
+  constexpr int TPR = D / 8;  // threads per row, 8 elements each
+  constexpr int RPB = kThreads / TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  if (row >= a.rows) return;
+  float m = -INFINITY;
+  for (int b = 0; b < a.n; ++b) m = fmaxf(m, a.lse[b][row]);
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (m != -INFINITY) {
+    for (int b = 0; b < a.n; ++b) {
+      const float l = a.lse[b][row];
+      if (l == -INFINITY) continue;
+      const float w = expf(l - m);
+      tot += w;
+      const f32x4* src = reinterpret_cast<const f32x4*>(a.o[b] + row * D + part * 8);
+      acc0 += w * src[0];
+      acc1 += w * src[1];
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  u32x4 w = {pack_bf16(acc0[0] * inv, acc0[1] * inv), pack_bf16(acc0[2] * inv, acc0[3] * inv),
+             pack_bf16(acc1[0] * inv, acc1[1] * inv), pack_bf16(acc1[2] * inv, acc1[3] * inv)};
+  *reinterpret_cast<u32x4*>(a.out + row * D + part * 8) = w;
+  if (part == 0) a.lse_out[row] = tot > 0.f ? m + logf(tot) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_merge(const float* const* o_parts, const float* const* lse_parts, int n, uint16_t* o,
+                        float* lse, long long rows, int D, hipStream_t stream) {
+  MergeArgs a;
+  for (int i = 0; i < kMaxMerge; ++i) {
+    a.o[i] = i < n ? o_parts[i] : nullptr;
+    a.lse[i] = i < n ? lse_parts[i] : nullptr;
+  }
+  a.n = n;
+  a.out = o;
+  a.lse_out = lse;
+  a.rows = rows;
+  const int rpb = kThreads / (D / 8);
+  const long long grid = (rows + rpb - 1) / rpb;
+  void* args[] = {&a};
+  const void* k = D == 128 ? reinterpret_cast<const void*>(&attn_merge_kernel<128>)
+                           : reinterpret_cast<const void*>(&attn_merge_kernel<64>);
+  return hipLaunchKernel(k, dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace tam
