@@ -125,6 +125,92 @@ def cpu_baseline(w, x, n_groups):
                       f"{dt:.1f} s wall; counted FLOPs of that sample"}
 
 
+def cp_bench(args, w):
+    """One rank of an N-way context-parallel split on this GPU: the last query block
+    (the heaviest under a causal mask) against all N key blocks, through the block
+    calls. Counted FLOPs are those of the rank's visible (query, key) pairs, with the
+    same forward and 2.5x backward factors as the whole-sequence metric."""
+    import numpy as np
+    import torch
+    import tiled_attention_memory_amd as tam
+    from tiled_attention_memory_amd import workloads as wl
+    n = args.cp
+    if w.S % n:
+        print(f"--cp {n} must divide S = {w.S}", file=sys.stderr)
+        sys.exit(2)
+    s = w.S // n
+    r = n - 1
+    x = wl.workload_inputs(w)
+    dev = {k_: torch.from_numpy(np.ascontiguousarray(x[k_]).view(np.int16)).view(torch.bfloat16).cuda()
+           for k_ in x}
+    q0 = r * s
+    qb = dev["q"][:, :, q0:q0 + s].contiguous()
+    dob = dev["do"][:, :, q0:q0 + s].contiguous()
+    kbs = [(dev["k"][:, :, b * s:(b + 1) * s].contiguous(), dev["v"][:, :, b * s:(b + 1) * s].contiguous())
+           for b in range(n)]
+    del dev
+    parts = [(torch.empty((w.B, w.Hq, s, w.D), dtype=torch.float32, device="cuda"),
+              torch.empty((w.B, w.Hq, s), dtype=torch.float32, device="cuda")) for _ in range(n)]
+    o = torch.empty_like(qb)
+    lse = torch.empty((w.B, w.Hq, s), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tam.attn_bwd_block_workspace_bytes(w.B, w.Hq, w.Hkv, s, s, w.D), dtype=torch.uint8,
+                     device="cuda")
+    dq = torch.empty_like(qb)
+    dks = [(torch.empty_like(kk), torch.empty_like(vv)) for kk, vv in kbs]
+    hip = Hip()
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def step(ev=None):
+        if ev:
+            hip.record(ev[0], sh)
+        for b, (kk, vv) in enumerate(kbs):
+            tam.attn_fwd_block(qb, kk, vv, parts[b][0], parts[b][1], q0, b * s, causal=True, scale=w.scale)
+        tam.attn_merge([p[0] for p in parts], [p[1] for p in parts], o, lse)
+        if ev:
+            hip.record(ev[1], sh)
+        tam.attn_bwd_block_begin(o, dob, lse, ws, w.Hkv, s)
+        for b, (kk, vv) in enumerate(kbs):
+            tam.attn_bwd_block_dq(qb, kk, vv, dob, ws, q0, b * s, causal=True, scale=w.scale)
+        tam.attn_bwd_block_dq_end(dq, ws, w.Hkv, s, scale=w.scale)
+        for b, (kk, vv) in enumerate(kbs):
+            tam.attn_bwd_block_dkdv(qb, kk, vv, dob, dks[b][0], dks[b][1], ws, q0, b * s, causal=True,
+                                    scale=w.scale)
+        if ev:
+            hip.record(ev[2], sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(hip.event(), hip.event(), hip.event()) for _ in range(K)]
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    fwd_ms = sum(hip.ms(e[0], e[1]) for e in evs) / K
+    bwd_ms = sum(hip.ms(e[1], e[2]) for e in evs) / K
+    for e in evs:
+        for h in e:
+            hip.destroy(h)
+    pairs = r * s * s + s * (s + 1) // 2            # visible (query, key) pairs of the rank, per head
+    fwd_flops = 4 * w.B * w.Hq * w.D * pairs
+    bwd_flops = 5 * fwd_flops // 2
+    ms_step = fwd_ms + bwd_ms
+    value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": f"attention fwd+bwd TFLOP/s, one rank of a {n}-way context-parallel split (block calls)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}_cp{n}_rank{r}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S,
+                   "D": w.D, "block": s, "causal": True},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +218,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2_70b_layer_s4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cp", type=int, default=0, metavar="N",
+                    help="instead of the whole-sequence step, time the last rank of an N-way "
+                         "context-parallel split of the workload: its query block against every key "
+                         "block (forward block calls + merge, then the block backward protocol)")
     ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
                     help="before each step, overwrite a MIB-mebibyte buffer so that L2 and the "
                          "memory-side cache start cold (for the short, bandwidth-bound shapes); "
@@ -158,6 +248,8 @@ def main():
     tam.load()  # fail loudly if the HIP library is missing
     w = wl.BY_NAME[args.workload]
     log(f"[bench] workload {w.name}: {w.describe()}")
+    if args.cp:
+        return cp_bench(args, w)
     x = wl.workload_inputs(w)
     dev = {n: torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(torch.bfloat16).cuda()
            for n in x}

@@ -163,3 +163,65 @@ def test_single_block_matches_attn_fwd_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
     assert torch.equal(lse, l_ref)
+
+
+def test_context_parallel_rank_at_full_size():
+    """The last of 8 ranks of the 81920-token workload: its 10240 query rows against
+    all 8 key blocks, forward (8 block calls + merge) and the backward protocol.
+
+    O, LSE and dQ of sampled rows against the whole-sequence oracle (a row's
+    results depend on its own score row only); dK and dV, summed over the key
+    blocks, through two exact properties of this query block's contribution:
+    sum_j dK_j = 0 (shifting every key leaves its outputs unchanged) and
+    sum_j dV_j = sum over its rows and the group's heads of dO.
+    """
+    import torch
+    import tiled_attention_memory_amd as tam
+    w = wl.BY_NAME["very_long_s81920"]
+    n = 8
+    s = w.S // n
+    r = n - 1
+    say(f"context-parallel rank {r} of {n}, {w.name}")
+    x = wl.workload_inputs(w)
+    q, k, v, do = (to_dev(x[nm]) for nm in ("q", "k", "v", "do"))
+    q0 = r * s
+    qb, dob = q[:, :, q0:q0 + s].contiguous(), do[:, :, q0:q0 + s].contiguous()
+    kbs = [(k[:, :, b * s:(b + 1) * s].contiguous(), v[:, :, b * s:(b + 1) * s].contiguous()) for b in range(n)]
+    parts = []
+    for b, (kk, vv) in enumerate(kbs):
+        o_p, l_p = _dev_f32((w.B, w.Hq, s, w.D)), _dev_f32((w.B, w.Hq, s))
+        tam.attn_fwd_block(qb, kk, vv, o_p, l_p, q0, b * s, causal=True, scale=w.scale)
+        parts.append((o_p, l_p))
+    o = torch.empty_like(qb)
+    lse = _dev_f32((w.B, w.Hq, s))
+    tam.attn_merge([p[0] for p in parts], [p[1] for p in parts], o, lse)
+    ws = torch.empty(tam.attn_bwd_block_workspace_bytes(w.B, w.Hq, w.Hkv, s, s, w.D), dtype=torch.uint8,
+                     device="cuda")
+    tam.attn_bwd_block_begin(o, dob, lse, ws, w.Hkv, s)
+    for b, (kk, vv) in enumerate(kbs):
+        tam.attn_bwd_block_dq(qb, kk, vv, dob, ws, q0, b * s, causal=True, scale=w.scale)
+    dq = torch.empty_like(qb)
+    tam.attn_bwd_block_dq_end(dq, ws, w.Hkv, s, scale=w.scale)
+    dk_sum = torch.zeros((w.B, w.Hkv, w.D), dtype=torch.float64, device="cuda")
+    dv_sum = torch.zeros_like(dk_sum)
+    for b, (kk, vv) in enumerate(kbs):
+        dk, dv = torch.empty_like(kk), torch.empty_like(vv)
+        tam.attn_bwd_block_dkdv(qb, kk, vv, dob, dk, dv, ws, q0, b * s, causal=True, scale=w.scale)
+        dk_sum += dk.double().sum(dim=2)
+        dv_sum += dv.double().sum(dim=2)
+    torch.cuda.synchronize()
+    say("oracle on sampled rows")
+    qh, kh, vh, doh = (_f64(x[nm]) for nm in ("q", "k", "v", "do"))
+    rng = np.random.default_rng(7)
+    rows = np.concatenate([np.arange(0, 64), np.arange(s - 64, s), rng.choice(s, 64, replace=False)])
+    go, gl, gq = to_f64(o), to_f64(lse), to_f64(dq)
+    for h in (0, 5):
+        ref = att.rows_forward_backward(qh[0, h], kh[0, 0], vh[0, 0], doh[0, h], q0 + rows, w.scale)
+        assert_close(f"o rows h{h}", go[0, h, rows], ref["o"])
+        assert_lse(gl[0, h, rows], ref["lse"])
+        assert_close(f"dq rows h{h}", gq[0, h, rows], ref["dq"])
+    dk_sum, dv_sum = dk_sum.cpu().numpy(), dv_sum.cpu().numpy()
+    do_sum = doh[:, :, q0:q0 + s].reshape(w.B, w.Hkv, w.group, s, w.D).sum(axis=(2, 3))
+    tol = 2e-2 * math.sqrt(w.S)
+    assert np.max(np.abs(dk_sum)) <= tol, np.max(np.abs(dk_sum))
+    assert np.max(np.abs(dv_sum - do_sum)) <= tol, np.max(np.abs(dv_sum - do_sum))
