@@ -211,6 +211,62 @@ def cp_bench(args, w):
     print(json.dumps(out), flush=True)
 
 
+def decode_bench(args, w):
+    """attn_decode on a synthetic cache (seeded N(0,1), like the training shapes).
+
+    Bound by HBM: the algorithmic bytes are the cache (K and V) read once plus the
+    new tokens' Q read and O, LSE written; value is those bytes over the call's time."""
+    import numpy as np
+    import torch
+    import tiled_attention_memory_amd as tam
+    from tiled_attention_memory_amd import workloads as wl
+    B, Sq, Sk = (int(t) for t in args.decode.split(","))
+    x = wl.make_inputs(B, w.Hq, w.Hkv, Sk, w.D, seed=(500, B, Sq, Sk))
+    dev = {n: torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(torch.bfloat16).cuda()
+           for n in ("q", "k", "v")}
+    q = dev["q"][:, :, Sk - Sq:].contiguous()
+    k, v = dev["k"], dev["v"]
+    del dev
+    o = torch.empty_like(q)
+    lse = torch.empty((B, w.Hq, Sq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tam.attn_decode_workspace_bytes(B, w.Hq, w.Hkv, Sq, Sk, w.D), dtype=torch.uint8,
+                     device="cuda")
+    flush = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda") if args.flush_mib else None)
+    hip = Hip()
+    sh = torch.cuda.current_stream().cuda_stream
+    for _ in range(args.warmup):
+        tam.attn_decode(q, k, v, o, lse, ws, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(hip.event(), hip.event()) for _ in range(K)]
+    for i in range(K):
+        if flush is not None:
+            flush.fill_(float(i))
+        hip.record(evs[i][0], sh)
+        tam.attn_decode(q, k, v, o, lse, ws, causal=True, scale=w.scale)
+        hip.record(evs[i][1], sh)
+    torch.cuda.synchronize()
+    ms = sum(hip.ms(a, b) for a, b in evs) / K
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    cache = 2 * B * w.Hkv * Sk * w.D * 2
+    qo = 2 * B * w.Hq * Sq * w.D * 2 + B * w.Hq * Sq * 4
+    gbps = (cache + qo) / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "attention decode GB/s (algorithmic bytes: cache read once, new tokens in and out)",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode_b{B}_q{Sq}_s{Sk}_h{w.Hq}x{w.Hkv}_d{w.D}", "B": B, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "Sq": Sq, "Sk": Sk, "D": w.D, "causal": True,
+                   "cache": "cold" if flush is not None else "warm"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +278,9 @@ def main():
                     help="instead of the whole-sequence step, time the last rank of an N-way "
                          "context-parallel split of the workload: its query block against every key "
                          "block (forward block calls + merge, then the block backward protocol)")
+    ap.add_argument("--decode", default="", metavar="B,SQ,SK",
+                    help="instead of the training step, time attn_decode: B sequences with SQ new tokens "
+                         "per head against an SK-key cache, with the workload's heads and head size")
     ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
                     help="before each step, overwrite a MIB-mebibyte buffer so that L2 and the "
                          "memory-side cache start cold (for the short, bandwidth-bound shapes); "
@@ -250,6 +309,8 @@ def main():
     log(f"[bench] workload {w.name}: {w.describe()}")
     if args.cp:
         return cp_bench(args, w)
+    if args.decode:
+        return decode_bench(args, w)
     x = wl.workload_inputs(w)
     dev = {n: torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(torch.bfloat16).cuda()
            for n in x}

@@ -1,5 +1,5 @@
 """C ABI contract on the CPU: the library loads, exports what include/attn.h and
-include/attn_block.h declare, and rejects every invalid argument before
+include/attn_block.h and include/attn_decode.h declare, and rejects every invalid argument before
 touching the GPU.
 
 Every call below fails validation, and validation happens before any HIP
@@ -14,7 +14,7 @@ import pytest
 import tiled_attention_memory_amd as tam
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("attn.h", "attn_block.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("attn.h", "attn_block.h", "attn_decode.h")]
 
 A = 1 << 20          # fake, 16-byte aligned, far-apart "device" addresses (never dereferenced)
 GOOD = dict(B=1, Hq=4, Hkv=2, S=128, D=128, causal=1, scale=0.125)
@@ -202,3 +202,27 @@ def test_block_backward_rejects():
                                    0.1, None) == 9    # dk and dv overlap
     assert lib.attn_bwd_block_dkdv(A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, W, need, B, Hq, Hkv, Sq, Sk + 512, D, 1,
                                    0, 0, 0.1, None) == 6    # workspace sized for a smaller key block
+
+
+# ---------------------------------------------------------------------------
+# decode (attn_decode.h): validation only
+# ---------------------------------------------------------------------------
+def test_decode_rejects():
+    lib = tam.load()
+    B, Hq, Hkv, Sq, Sk, D = 2, 8, 2, 4, 1000, 128
+    need = tam.attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
+    W = 64 * A
+    ok = (A, 2 * A, 3 * A, 4 * A, 5 * A, W, need)
+    assert lib.attn_decode(*ok, B, Hq, Hkv, 33, Sk, D, 1, 0.1, None) == 2        # g * Sq = 132 > 128
+    assert lib.attn_decode(*ok, B, Hq, Hkv, Sq, 3, D, 1, 0.1, None) == 2         # Sq > Sk
+    assert lib.attn_decode(*ok, B, 6, 4, Sq, Sk, D, 1, 0.1, None) == 2           # Hq % Hkv
+    assert lib.attn_decode(*ok, B, Hq, Hkv, Sq, Sk, 80, 1, 0.1, None) == 3
+    assert lib.attn_decode(*ok, B, Hq, Hkv, Sq, Sk, D, 5, 0.1, None) == 8
+    assert lib.attn_decode(*ok, B, Hq, Hkv, Sq, Sk, D, 1, float("inf"), None) == 4
+    assert lib.attn_decode(A, 2 * A, 3 * A, 4 * A, 5 * A, W, need - 1, B, Hq, Hkv, Sq, Sk, D, 1, 0.1, None) == 6
+    assert lib.attn_decode(A, 2 * A, 3 * A, A + 64, 5 * A, W, need, B, Hq, Hkv, Sq, Sk, D, 1, 0.1, None) == 9
+    assert lib.attn_decode(A, 2 * A + 2, 3 * A, 4 * A, 5 * A, W, need, B, Hq, Hkv, Sq, Sk, D, 1, 0.1, None) == 5
+    assert lib.attn_decode(0, 2 * A, 3 * A, 4 * A, 5 * A, W, need, B, Hq, Hkv, Sq, Sk, D, 1, 0.1, None) == 1
+    with pytest.raises(tam.AttnError):
+        tam.attn_decode_workspace_bytes(B, Hq, Hkv, 33, Sk, D)                    # g * Sq = 132 > 128
+    assert tam.attn_decode_workspace_bytes(1, 64, 8, 16, 4096, 128) > 0

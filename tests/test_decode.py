@@ -1,0 +1,73 @@
+"""GPU parity of decoding against a key/value cache (include/attn_decode.h).
+
+The new tokens sit at the last Sq positions of the cache; the expected output
+is the block oracle (oracle.blocks) for that query block against the whole
+cache, which in turn is pinned to the whole-sequence oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from gpu_helpers import assert_close, assert_lse, say, to_dev, to_f64
+from oracle import attention as att
+from oracle import blocks as blk
+from tiled_attention_memory_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(x, Sq, causal, scale):
+    import torch
+    import tiled_attention_memory_amd as tam
+    B, Hq, S, D = x["q"].shape
+    Hkv = x["k"].shape[1]
+    q = to_dev(x["q"][:, :, S - Sq:])
+    k, v = to_dev(x["k"]), to_dev(x["v"])
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tam.attn_decode_workspace_bytes(B, Hq, Hkv, Sq, S, D), dtype=torch.uint8, device="cuda")
+    tam.attn_decode(q, k, v, o, lse, ws, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return to_f64(o), to_f64(lse)
+
+
+CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal
+    (2, 8, 2, 1, 1000, 128, True),
+    (1, 64, 8, 4, 4096, 128, True),     # 8 heads x 4 tokens = 32 packed rows per group
+    (1, 32, 8, 16, 3001, 128, True),    # 4 x 16 = 64 rows, ragged cache
+    (3, 16, 1, 8, 777, 64, True),       # 16 x 8 = 128 rows (the limit), D = 64
+    (1, 4, 4, 5, 5, 128, True),         # the whole sequence is new
+    (2, 8, 2, 3, 2048, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_Sq{}_Sk{}_D{}_{}".format(
+    *c[:6], "causal" if c[6] else "full"))
+def test_decode_against_oracle(case):
+    B, Hq, Hkv, Sq, Sk, D, causal = case
+    say(f"decode {case}")
+    x = wl.make_inputs(B, Hq, Hkv, Sk, D, seed=(400, Sq, Sk, D))
+    scale = 1.0 / math.sqrt(D)
+    go, gl = run_decode(x, Sq, causal, scale)
+    q, k, v = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v"))
+    ro, rl = blk.forward_block(q[:, :, Sk - Sq:], k, v, scale, causal, Sk - Sq, 0)
+    assert_close("o", go, ro)
+    assert_lse(gl, rl)
+
+
+def test_decode_matches_last_rows_of_the_forward_pass():
+    """Decoding the last 4 tokens equals the last 4 rows of attn_fwd on the whole sequence."""
+    import torch
+    import tiled_attention_memory_amd as tam
+    say("decode vs attn_fwd rows")
+    B, Hq, Hkv, S, D, Sq = 1, 16, 4, 1500, 128, 4
+    x = wl.make_inputs(B, Hq, Hkv, S, D, seed=(401,))
+    go, gl = run_decode(x, Sq, True, 1.0 / math.sqrt(D))
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    o, lse = tam.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    # two different reductions of the same exact values: within rounding of each other
+    assert np.max(np.abs(go - to_f64(o)[:, :, S - Sq:])) <= 2e-2
+    assert np.max(np.abs(gl - to_f64(lse)[:, :, S - Sq:])) <= 1e-4

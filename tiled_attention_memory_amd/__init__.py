@@ -1,6 +1,6 @@
 """Exact causal GQA attention for MI355X (gfx950): HIP kernels behind a C ABI.
 
-The Python names mirror include/attn.h and include/attn_block.h. The library is loaded on first use
+The Python names mirror include/attn.h, include/attn_block.h and include/attn_decode.h. The library is loaded on first use
 and every call fails loudly if it is missing; nothing here computes attention.
 """
 from ._binding import (  # noqa: F401
@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     attn_bwd_block_dq,
     attn_bwd_block_dq_end,
     attn_bwd_block_workspace_bytes,
+    attn_decode,
+    attn_decode_workspace_bytes,
     attn_fwd_block,
     attn_merge,
     attn_bwd,

@@ -1,7 +1,7 @@
 """ctypes binding of libattn.so: argument marshalling only.
 
 Every computation happens in the HIP kernels behind the C ABI declared in
-include/attn.h and include/attn_block.h. PyTorch is used only to own device memory and to provide the
+include/attn.h, include/attn_block.h and include/attn_decode.h. PyTorch is used only to own device memory and to provide the
 stream handle. There is no fallback: if the library is missing, every call
 raises.
 """
@@ -23,7 +23,8 @@ STATUS = {
 
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_bwd_workspace_bytes", "attn_status_string",
            "attn_version", "attn_fwd_block", "attn_merge", "attn_bwd_block_workspace_bytes",
-           "attn_bwd_block_begin", "attn_bwd_block_dq", "attn_bwd_block_dq_end", "attn_bwd_block_dkdv")
+           "attn_bwd_block_begin", "attn_bwd_block_dq", "attn_bwd_block_dq_end", "attn_bwd_block_dkdv",
+           "attn_decode_workspace_bytes", "attn_decode")
 BWD_EVENTS = 5
 MAX_MERGE = 16
 
@@ -70,8 +71,11 @@ def load() -> ctypes.CDLL:
         lib.attn_bwd_block_dq.argtypes = [vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, ll, ll, f, vp]
         lib.attn_bwd_block_dq_end.argtypes = [vp, vp, sz, i, i, i, i, i, i, f, vp]
         lib.attn_bwd_block_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, ll, ll, f, vp]
+        lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(sz)]
+        lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
         for name in ("attn_fwd_block", "attn_merge", "attn_bwd_block_workspace_bytes", "attn_bwd_block_begin",
-                     "attn_bwd_block_dq", "attn_bwd_block_dq_end", "attn_bwd_block_dkdv"):
+                     "attn_bwd_block_dq", "attn_bwd_block_dq_end", "attn_bwd_block_dkdv",
+                     "attn_decode_workspace_bytes", "attn_decode"):
             getattr(lib, name).restype = i
         _lib = lib
         return lib
@@ -309,3 +313,25 @@ def attn_bwd_block_dkdv(q, k, v, dout, dk, dv, workspace, q_pos0, k_pos0, causal
     _raise(load().attn_bwd_block_dkdv(*p, *_ws_ptr(workspace), B, Hq, Hkv, Sq, Sk, D, int(bool(causal)),
                                       int(q_pos0), int(k_pos0), _scale(scale, D), _stream(stream)),
            "attn_bwd_block_dkdv")
+
+
+# ---------------------------------------------------------------------------
+# decode against a key/value cache (include/attn_decode.h)
+# ---------------------------------------------------------------------------
+def attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, D: int) -> int:
+    out = ctypes.c_size_t(0)
+    _raise(load().attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, ctypes.byref(out)),
+           "attn_decode_workspace_bytes")
+    return out.value
+
+
+def attn_decode(q, k, v, o, lse, workspace, causal=True, scale=None, stream=None) -> None:
+    """Sq new tokens per head (the last Sq positions) against the Sk-key cache k, v."""
+    import torch
+    B, Hq, Hkv, Sq, Sk, D = _block_shape(q, k)
+    bf = torch.bfloat16
+    p = [_check(q, "q", bf, (B, Hq, Sq, D)), _check(k, "k", bf, (B, Hkv, Sk, D)),
+         _check(v, "v", bf, (B, Hkv, Sk, D)), _check(o, "o", bf, (B, Hq, Sq, D)),
+         _check(lse, "lse", torch.float32, (B, Hq, Sq))]
+    _raise(load().attn_decode(*p, *_ws_ptr(workspace), B, Hq, Hkv, Sq, Sk, D, int(bool(causal)),
+                              _scale(scale, D), _stream(stream)), "attn_decode")

@@ -1,8 +1,9 @@
 // C ABI of libattn.so: argument validation, then dispatch to the kernels.
 // The contract (layout, ownership, error behaviour) is stated in include/attn.h
-// and include/attn_block.h.
+// include/attn_block.h and include/attn_decode.h.
 #include "attn.h"
 #include "attn_block.h"
+#include "attn_decode.h"
 
 #include <math.h>
 #include <stdint.h>
@@ -318,6 +319,61 @@ ATTN_EXPORT int attn_bwd_block_dkdv(const void* q, const void* k, const void* v,
                                                static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout),
                                                static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), workspace,
                                                stream));
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode against a key/value cache (attn_decode.h)
+// ---------------------------------------------------------------------------
+namespace {
+int check_decode(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
+  int st = check_shape(B, Hq, Hkv, Sq, Sk, D);
+  if (st != ATTN_OK) return st;
+  if (Sq > Sk || (long long)(Hq / Hkv) * Sq > 128) return ATTN_ERR_BAD_SHAPE;
+  return ATTN_OK;
+}
+tam::AttnShape decode_shape(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale) {
+  return tam::AttnShape{B, Hq, Hkv, Sq, Sk, D, causal != 0, Sk - Sq, scale};
+}
+}  // namespace
+
+ATTN_EXPORT int attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, size_t* bytes) {
+  if (!bytes) return ATTN_ERR_NULL_POINTER;
+  const int st = check_decode(B, Hq, Hkv, Sq, Sk, D);
+  if (st != ATTN_OK) return st;
+  *bytes = tam::decode_workspace_bytes(decode_shape(B, Hq, Hkv, Sq, Sk, D, 1, 1.f));
+  return ATTN_OK;
+}
+
+ATTN_EXPORT int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                            size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                            float scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_POINTER;
+  int st = check_decode(B, Hq, Hkv, Sq, Sk, D);
+  if (st != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return ATTN_ERR_BAD_FLAG;
+  if (!isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_MISALIGNED;
+  const tam::AttnShape sh = decode_shape(B, Hq, Hkv, Sq, Sk, D, causal, scale);
+  const size_t need = tam::decode_workspace_bytes(sh);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_MISALIGNED;
+  const size_t qb = (size_t)B * Hq * Sq * D * 2, kb = (size_t)B * Hkv * Sk * D * 2, lb = (size_t)B * Hq * Sq * 4;
+  const Range ins[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
+  const Range outs[] = {range_of(o, qb), range_of(lse, lb), range_of(workspace, need)};
+  for (int i = 0; i < 3; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return ATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return ATTN_ERR_ALIAS;
+  }
+  try {
+    return from_hip(tam::launch_decode(sh, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, workspace,
+                                       stream));
   } catch (...) {
     return ATTN_ERR_HIP;
   }

@@ -316,11 +316,11 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
         float ds[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x4 dlt = *reinterpret_cast<const f32x4*>(Fs + kKBR + qs * 32 + 8 * i + 4 * half);
+          const f32x4 dl4 = *reinterpret_cast<const f32x4*>(Fs + kKBR + qs * 32 + 8 * i + 4 * half);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int v = 4 * i + r;
-            ds[v] = pbuf[(16 * qs + v) * 64] * (x[qs][v] - dlt[r]);
+            ds[v] = pbuf[(16 * qs + v) * 64] * (x[qs][v] - dl4[r]);
           }
         }
 #pragma unroll

@@ -47,6 +47,13 @@ struct FwdArgs {
   float* lse;
   int Hq, Hkv, Sq, Sk, dlt;
   float c;  // softmax scale * log2(e): scores are exponentiated in base 2
+  // Packed rows (decode): pack > 0 is the group size g, a unit holds the Sq
+  // tokens of all g query heads of one kv head (row r = head r / Sq, token
+  // r % Sq; g * Sq <= 128), its tile index is a split of the keys into chunks
+  // of kv_chunk, and split s writes its fp32 partials at o32 + s * o_stride and
+  // lse + s * lse_stride.
+  int pack, kv_chunk;
+  long long o_stride, lse_stride;
   TileSched sched;
 };
 
@@ -76,14 +83,38 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
   const int col = lane & 31, half = lane >> 5;
   const int Sq = a.Sq, Sk = a.Sk, dlt = a.dlt;
-  const int b = bh / a.Hq, h = bh - b * a.Hq;
-  const int kvh = h / (a.Hq / a.Hkv);
-  const size_t q_base = (size_t)bh * Sq * D;
+  const bool packed = a.pack > 0;
+  const int r = wave * 32 + col;     // the row of the unit this lane owns
+  int b, kvh, tok, w_tmin, w_tmax, t_last, kbeg, kend, split = 0;
+  bool row_ok;
+  size_t row_off;                    // element offset of this lane's row in q, o (and / D in lse)
+  if (packed) {                      // unit = (batch, kv head, key split)
+    b = bh / a.Hkv;
+    kvh = bh - b * a.Hkv;
+    split = qt;
+    const int hoff = r / Sq;
+    tok = r - hoff * Sq;
+    row_ok = hoff < a.pack;
+    row_off = ((size_t)(b * a.Hq + kvh * a.pack + hoff) * Sq + tok) * D;
+    w_tmin = 0;
+    w_tmax = Sq - 1;
+    t_last = Sq - 1;
+    kbeg = split * a.kv_chunk;
+    kend = min(Sk, kbeg + a.kv_chunk);
+  } else {                           // unit = (batch, query head, 128-row tile)
+    b = bh / a.Hq;
+    kvh = (bh - b * a.Hq) / (a.Hq / a.Hkv);
+    tok = qt * kBR + r;
+    row_ok = tok < Sq;
+    row_off = ((size_t)bh * Sq + tok) * D;
+    w_tmin = qt * kBR + wave * 32;   // the wave's first row
+    w_tmax = w_tmin + 31;
+    t_last = min(qt * kBR + kBR, Sq) - 1;
+    kbeg = 0;
+    kend = Sk;
+  }
   const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)Sk * D;
   const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)Sk * D;
-  const int q0 = qt * kBR;
-  const int wrow0 = q0 + wave * 32;  // first query row of this wave
-  const int qrow = wrow0 + col;      // the query row this lane owns
 
   // Q rows as MFMA B operands (k = head dim), resident for the whole loop. A
   // negative scale is folded into Q (an exact sign flip), so the softmax below
@@ -91,11 +122,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const float c = fabsf(a.c);
   bf16x8 qf[KS];
   {
-    const uint16_t* qp = a.q + q_base + (size_t)qrow * D + 8 * half;
+    const uint16_t* qp = a.q + row_off + 8 * half;
     const uint32_t flip = a.c < 0.f ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 w = qrow < Sq ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      u32x4 w = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
       w ^= flip;
       qf[ks] = __builtin_bit_cast(bf16x8, w);
     }
@@ -119,10 +150,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NLD; ++i) loff[i] = T::load_src(wave * NLD + i, lane);
 
-  const int last_row = min(q0 + kBR, Sq) - 1;
-  const int n_kv = (Sk + kBC - 1) / kBC;
-  // the last key any row of the unit may see is last_row + dlt
-  const int ntiles = CAUSAL ? (last_row + dlt < 0 ? 0 : min(n_kv, (last_row + dlt) / kBC + 1)) : n_kv;
+  // key tiles [jbeg, jend) of the unit's key range; the last key any row of
+  // the unit may see is t_last + dlt
+  const int jbeg = kbeg / kBC;
+  const int n_kv = (kend + kBC - 1) / kBC;
+  const int jend = CAUSAL ? (t_last + dlt < kbeg ? jbeg : min(n_kv, (t_last + dlt) / kBC + 1)) : n_kv;
 
   // K and V tile j straight into an LDS stage; rows past S read as zeros.
   auto issue = [&](int j, unsigned char* stage) TAM_INLINE {
@@ -157,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     const unsigned char* Vs = cur + T::BYTES + KB0 * 32 * T::ROW_BYTES;
 
     // S^T for the 32-key blocks: lane holds keys kv0 + 32(KB0 + kb) + 8(v/4) + 4half + v%4
-    // of row qrow; independent accumulator chains, interleaved
+    // of this lane's row; independent accumulator chains, interleaved
     f32x16 s[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
@@ -170,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     // Whether this row may see the key of accumulator element v of block kb:
     // that key is kv0 + 32 KB0 + 4half + off with the constant
     // off = 32kb + 8(v/4) + v%4, so one compare against a per-lane limit decides it.
-    const int lim = (CAUSAL ? min(qrow + dlt, Sk - 1) : Sk - 1) - (kv0 + 32 * KB0 + 4 * half);
+    const int lim = (CAUSAL ? min(tok + dlt, kend - 1) : kend - 1) - (kv0 + 32 * KB0 + 4 * half);
     auto visible = [&](int kb, int v) TAM_INLINE { return kb * 32 + 8 * (v >> 2) + (v & 3) <= lim; };
     if (MASKED) {
 #pragma unroll
@@ -244,9 +276,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 
   // Tile j on stage cur while tile j + 1 loads into nxt; one barrier per tile
   // for every wave, whichever loop below runs it.
+  // a wave whose rows are all padding (packed rows fewer than 128) only loads
+  const bool wave_rows = !packed || wave * 32 < a.pack * Sq;
   auto step = [&](auto masked_tag, int j, const unsigned char* cur, unsigned char* nxt) TAM_INLINE {
-    if (j + 1 < ntiles) issue(j + 1, nxt);
-    tile(masked_tag, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, j * kBC, cur);
+    if (j + 1 < jend) issue(j + 1, nxt);
+    if (wave_rows)
+      tile(masked_tag, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, j * kBC, cur);
     wait_loads();
     __syncthreads();
   };
@@ -254,12 +289,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   // Leading tiles lie entirely below this wave's diagonal and inside the
   // sequence: they run unmasked, two per iteration with fixed stages. The
   // remaining few tiles (diagonal, ragged end) run one by one.
-  const int n_plain = max(0, min(ntiles, (CAUSAL ? min(wrow0 + dlt + 1, Sk) : Sk) / kBC));
-  if (ntiles > 0) issue(0, stage0);
+  const int jplain = max(jbeg, min(jend, (CAUSAL ? min(w_tmin + dlt + 1, kend) : kend) / kBC));
+  if (jend > jbeg) issue(jbeg, stage0);
   wait_loads();
   __syncthreads();
-  int j = 0;
-  for (; j + 2 <= n_plain; j += 2) {
+  int j = jbeg;
+  for (; j + 2 <= jplain; j += 2) {
     step(std::false_type{}, j, stage0, stage1);
     step(std::false_type{}, j + 1, stage1, stage0);
   }
@@ -269,37 +304,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     constexpr int STG = decltype(stage_tag)::value;
     const unsigned char* cur = STG ? stage1 : stage0;
     unsigned char* nxt = STG ? stage0 : stage1;
-    if (jj + 1 < ntiles) issue(jj + 1, nxt);
+    if (jj + 1 < jend) issue(jj + 1, nxt);
     const int kv0 = jj * kBC;
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
     using C2 = std::integral_constant<int, 2>;
-    if (!CAUSAL || kv0 <= wrow0 + 31 + dlt) {   // some key of the tile is visible to this wave
-      if (jj < n_plain) {
+    if (wave_rows && (!CAUSAL || kv0 <= w_tmax + dlt)) {   // some key of the tile is visible to this wave
+      if (jj < jplain) {
         tile(std::false_type{}, C0{}, C2{}, kv0, cur);
       } else {
         tile(std::true_type{}, C0{}, C1{}, kv0, cur);
         // the second 32-key block, unless this wave sees none of its keys
-        if ((!CAUSAL || kv0 + 32 <= wrow0 + 31 + dlt) && kv0 + 32 < Sk) tile(std::true_type{}, C1{}, C1{}, kv0, cur);
+        if ((!CAUSAL || kv0 + 32 <= w_tmax + dlt) && kv0 + 32 < kend) tile(std::true_type{}, C1{}, C1{}, kv0, cur);
       }
     }
     wait_loads();
     __syncthreads();
   };
-  for (; j < ntiles; ++j) {
-    if (j & 1)
+  for (; j < jend; ++j) {
+    if ((j - jbeg) & 1)
       tail_step(std::integral_constant<int, 1>{}, j);
     else
       tail_step(std::integral_constant<int, 0>{}, j);
   }
 
   const float l_tot = sum_halves(l_run);
-  if (qrow < Sq) {
+  if (row_ok) {
     // a row that saw no key (possible with offset blocks) gets O = 0, LSE = -inf
     const bool seen = l_tot > 0.f;
     const float inv = seen ? 1.f / l_tot : 0.f;
     if (a.o32) {
-      float* op = a.o32 + q_base + (size_t)qrow * D + 4 * half;
+      float* op = a.o32 + split * a.o_stride + row_off + 4 * half;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -309,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     } else {
       // lane holds columns 32db + 8i + 4half + (0..3); pairs of i are merged
       // across the halves so each store writes 16 contiguous bytes per lane
-      uint16_t* op = a.o + q_base + (size_t)qrow * D + 8 * half;
+      uint16_t* op = a.o + row_off + 8 * half;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -324,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
           *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
         }
     }
-    if (half == 0) a.lse[(size_t)bh * Sq + qrow] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (half == 0) a.lse[split * a.lse_stride + row_off / D] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -343,6 +378,9 @@ hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, con
   a.Sq = sh.Sq;
   a.Sk = sh.Sk;
   a.dlt = sh.dlt;
+  a.pack = 0;
+  a.kv_chunk = 0;
+  a.o_stride = a.lse_stride = 0;
   a.c = sh.scale * kLog2e;
   a.sched.BH = sh.B * sh.Hq;
   a.sched.NT = (sh.Sq + kBR - 1) / kBR;
@@ -353,7 +391,70 @@ hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, con
                          dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_decode_t(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           uint16_t* o, float* lse, void* workspace, hipStream_t stream) {
+  const DecodePlan p = decode_plan(sh);
+  const long long rows = (long long)sh.B * sh.Hq * sh.Sq;
+  float* parts = static_cast<float*>(workspace);
+  float* lparts = parts + (size_t)p.splits * rows * sh.D;
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = nullptr;
+  a.o32 = parts;
+  a.lse = lparts;
+  a.Hq = sh.Hq;
+  a.Hkv = sh.Hkv;
+  a.Sq = sh.Sq;
+  a.Sk = sh.Sk;
+  a.dlt = sh.dlt;
+  a.pack = sh.Hq / sh.Hkv;
+  a.kv_chunk = p.chunk;
+  a.o_stride = rows * sh.D;
+  a.lse_stride = rows;
+  a.c = sh.scale * kLog2e;
+  a.sched.BH = sh.B * sh.Hkv;
+  a.sched.NT = p.splits;
+  a.sched.chunk = (a.sched.BH + 7) / 8;
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL>),
+                                 dim3((unsigned)sched_grid(a.sched)), dim3(kThreads), args, 0, stream);
+  if (e != hipSuccess) return e;
+  return launch_merge_strided(parts, lparts, p.splits, rows * sh.D, rows, o, lse, rows, sh.D, stream);
+}
+
 }  // namespace
+
+// Decode splits: enough (kv head, split) units to give every CU two
+// workgroups, but no split shorter than 256 keys.
+DecodePlan decode_plan(const AttnShape& sh) {
+  const long long units = (long long)sh.B * sh.Hkv;
+  long long want = (512 + units - 1) / units;
+  const long long by_keys = (sh.Sk + 255) / 256;
+  if (want > by_keys) want = by_keys;
+  if (want < 1) want = 1;
+  const int chunk = (int)(((sh.Sk + want - 1) / want + kBC - 1) / kBC * kBC);
+  DecodePlan p;
+  p.chunk = chunk;
+  p.splits = (sh.Sk + chunk - 1) / chunk;
+  return p;
+}
+
+size_t decode_workspace_bytes(const AttnShape& sh) {
+  const DecodePlan p = decode_plan(sh);
+  const size_t rows = (size_t)sh.B * sh.Hq * sh.Sq;
+  return (size_t)p.splits * rows * (sh.D + 1) * 4;
+}
+
+hipError_t launch_decode(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                         float* lse, void* workspace, hipStream_t stream) {
+  if (sh.D == 128) return sh.causal ? launch_decode_t<128, true>(sh, q, k, v, o, lse, workspace, stream)
+                                    : launch_decode_t<128, false>(sh, q, k, v, o, lse, workspace, stream);
+  return sh.causal ? launch_decode_t<64, true>(sh, q, k, v, o, lse, workspace, stream)
+                   : launch_decode_t<64, false>(sh, q, k, v, o, lse, workspace, stream);
+}
 
 hipError_t launch_fwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       uint16_t* o, float* o32, float* lse, hipStream_t stream) {

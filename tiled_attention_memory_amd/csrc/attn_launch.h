@@ -27,6 +27,20 @@ hipError_t launch_fwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
 
 hipError_t launch_merge(const float* const* o_parts, const float* const* lse_parts, int n, uint16_t* o,
                         float* lse, long long rows, int D, hipStream_t stream);
+// Part b at o_base + b * o_stride and lse_base + b * lse_stride (any n >= 1).
+hipError_t launch_merge_strided(const float* o_base, const float* lse_base, int n, long long o_stride,
+                                long long lse_stride, uint16_t* o, float* lse, long long rows, int D,
+                                hipStream_t stream);
+
+// Decode: Sq new tokens of every query head against Sk cached keys, split
+// over the keys; dlt = Sk - Sq places the tokens at the end of the cache.
+struct DecodePlan {
+  int splits, chunk;
+};
+DecodePlan decode_plan(const AttnShape& sh);
+size_t decode_workspace_bytes(const AttnShape& sh);
+hipError_t launch_decode(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                         float* lse, void* workspace, hipStream_t stream);
 
 // Workspace layout of the backward pass (bytes, 256-aligned offsets).
 size_t bwd_workspace_bytes(const AttnShape& sh);

@@ -22,8 +22,11 @@ namespace {
 constexpr int kThreads = 256;
 
 struct MergeArgs {
-  const float* o[kMaxMerge];
+  const float* o[kMaxMerge];     // part pointers, or
   const float* lse[kMaxMerge];
+  const float* o_base;           // (when set) part b at o_base + b * o_stride
+  const float* lse_base;
+  long long o_stride, lse_stride;
   int n;
   uint16_t* out;
   float* lse_out;
@@ -38,16 +41,18 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(MergeArgs a) {
   const int part = threadIdx.x % TPR;
   if (row >= a.rows) return;
   float m = -INFINITY;
-  for (int b = 0; b < a.n; ++b) m = fmaxf(m, a.lse[b][row]);
+  auto lse_of = [&](int b) { return a.lse_base ? a.lse_base + b * a.lse_stride : a.lse[b]; };
+  auto o_of = [&](int b) { return a.o_base ? a.o_base + b * a.o_stride : a.o[b]; };
+  for (int b = 0; b < a.n; ++b) m = fmaxf(m, lse_of(b)[row]);
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (m != -INFINITY) {
     for (int b = 0; b < a.n; ++b) {
-      const float l = a.lse[b][row];
+      const float l = lse_of(b)[row];
       if (l == -INFINITY) continue;
       const float w = expf(l - m);
       tot += w;
-      const f32x4* src = reinterpret_cast<const f32x4*>(a.o[b] + row * D + part * 8);
+      const f32x4* src = reinterpret_cast<const f32x4*>(o_of(b) + row * D + part * 8);
       acc0 += w * src[0];
       acc1 += w * src[1];
     }
@@ -59,16 +64,7 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(MergeArgs a) {
   if (part == 0) a.lse_out[row] = tot > 0.f ? m + logf(tot) : -INFINITY;
 }
 
-}  // namespace
-
-hipError_t launch_merge(const float* const* o_parts, const float* const* lse_parts, int n, uint16_t* o,
-                        float* lse, long long rows, int D, hipStream_t stream) {
-  MergeArgs a;
-  for (int i = 0; i < kMaxMerge; ++i) {
-    a.o[i] = i < n ? o_parts[i] : nullptr;
-    a.lse[i] = i < n ? lse_parts[i] : nullptr;
-  }
-  a.n = n;
+hipError_t merge(MergeArgs& a, uint16_t* o, float* lse, long long rows, int D, hipStream_t stream) {
   a.out = o;
   a.lse_out = lse;
   a.rows = rows;
@@ -78,6 +74,34 @@ hipError_t launch_merge(const float* const* o_parts, const float* const* lse_par
   const void* k = D == 128 ? reinterpret_cast<const void*>(&attn_merge_kernel<128>)
                            : reinterpret_cast<const void*>(&attn_merge_kernel<64>);
   return hipLaunchKernel(k, dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_merge(const float* const* o_parts, const float* const* lse_parts, int n, uint16_t* o,
+                        float* lse, long long rows, int D, hipStream_t stream) {
+  MergeArgs a;
+  for (int i = 0; i < kMaxMerge; ++i) {
+    a.o[i] = i < n ? o_parts[i] : nullptr;
+    a.lse[i] = i < n ? lse_parts[i] : nullptr;
+  }
+  a.o_base = a.lse_base = nullptr;
+  a.o_stride = a.lse_stride = 0;
+  a.n = n;
+  return merge(a, o, lse, rows, D, stream);
+}
+
+hipError_t launch_merge_strided(const float* o_base, const float* lse_base, int n, long long o_stride,
+                                long long lse_stride, uint16_t* o, float* lse, long long rows, int D,
+                                hipStream_t stream) {
+  MergeArgs a;
+  for (int i = 0; i < kMaxMerge; ++i) a.o[i] = a.lse[i] = nullptr;
+  a.o_base = o_base;
+  a.lse_base = lse_base;
+  a.o_stride = o_stride;
+  a.lse_stride = lse_stride;
+  a.n = n;
+  return merge(a, o, lse, rows, D, stream);
 }
 
 }  // namespace tam
