@@ -281,6 +281,9 @@ def main():
     ap.add_argument("--decode", default="", metavar="B,SQ,SK",
                     help="instead of the training step, time attn_decode: B sequences with SQ new tokens "
                          "per head against an SK-key cache, with the workload's heads and head size")
+    ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
+                    help="run the step with dropout probability P on the probabilities "
+                         "(attn_fwd_dropout / attn_bwd_dropout); the headline runs without")
     ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
                     help="before each step, overwrite a MIB-mebibyte buffer so that L2 and the "
                          "memory-side cache start cold (for the short, bandwidth-bound shapes); "
@@ -325,11 +328,24 @@ def main():
     def step(ev_f=None, ev_b=None):
         if ev_f:
             hip.record(ev_f[0], sh)
-        tam.attn_fwd(q, k, v, o, lse, causal=True, scale=w.scale, stream=stream)
+        if args.dropout:
+            tam.attn_fwd_dropout(q, k, v, o, lse, args.dropout, 1234, causal=True, scale=w.scale, stream=stream)
+        else:
+            tam.attn_fwd(q, k, v, o, lse, causal=True, scale=w.scale, stream=stream)
         if ev_f:
             hip.record(ev_f[1], sh)
-        tam.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=True, scale=w.scale,
-                     stream=stream, events=ev_b)
+        if args.dropout:
+            # no per-kernel events on this path: the whole backward pass is bracketed instead
+            if ev_b:
+                hip.record(ev_b[0], sh)
+            tam.attn_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, ws, args.dropout, 1234, causal=True,
+                                 scale=w.scale, stream=stream)
+            if ev_b:
+                for i in range(1, tam.BWD_EVENTS):
+                    hip.record(ev_b[i], sh)
+        else:
+            tam.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal=True, scale=w.scale,
+                         stream=stream, events=ev_b)
 
     hip = Hip()
     for _ in range(args.warmup):
@@ -420,8 +436,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
-                   "causal": True, "global_batch": w.B, "seq_len": w.S, "parallelism": "none"},
+        "config": {"workload": w.name + (f"_dropout{args.dropout:g}" if args.dropout else ""), "B": w.B,
+                   "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D, "causal": True, "global_batch": w.B,
+                   "seq_len": w.S, "parallelism": "none", **({"dropout": args.dropout} if args.dropout else {})},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(w.fwd_flops() / (per["attn_fwd_kernel"] * 1e-3) / 1e12, 1),
         "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),

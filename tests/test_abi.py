@@ -1,5 +1,5 @@
 """C ABI contract on the CPU: the library loads, exports what include/attn.h and
-include/attn_block.h and include/attn_decode.h declare, and rejects every invalid argument before
+include/attn_block.h, include/attn_decode.h and include/attn_dropout.h declare, and rejects every invalid argument before
 touching the GPU.
 
 Every call below fails validation, and validation happens before any HIP
@@ -14,7 +14,7 @@ import pytest
 import tiled_attention_memory_amd as tam
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("attn.h", "attn_block.h", "attn_decode.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("attn.h", "attn_block.h", "attn_decode.h", "attn_dropout.h")]
 
 A = 1 << 20          # fake, 16-byte aligned, far-apart "device" addresses (never dereferenced)
 GOOD = dict(B=1, Hq=4, Hkv=2, S=128, D=128, causal=1, scale=0.125)
@@ -226,3 +226,22 @@ def test_decode_rejects():
     with pytest.raises(tam.AttnError):
         tam.attn_decode_workspace_bytes(B, Hq, Hkv, 33, Sk, D)                    # g * Sq = 132 > 128
     assert tam.attn_decode_workspace_bytes(1, 64, 8, 16, 4096, 128) > 0
+
+
+# ---------------------------------------------------------------------------
+# dropout (attn_dropout.h): validation only
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("p", [-0.1, 0.999, 1.0, float("nan"), float("inf")])
+def test_dropout_rejects_bad_probability(p):
+    lib = tam.load()
+    assert lib.attn_fwd_dropout(A, 2 * A, 3 * A, 4 * A, 5 * A, 1, 4, 2, 128, 128, 1, 0.1, p, 7, None) == 4
+    need = tam.attn_bwd_workspace_bytes(1, 4, 2, 128, 128)
+    assert lib.attn_bwd_dropout(A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, 8 * A, 9 * A, 16 * A, need, 1, 4, 2, 128,
+                                128, 1, 0.1, p, 7, None) == 4
+
+
+def test_dropout_other_errors_match_attn_fwd():
+    lib = tam.load()
+    assert lib.attn_fwd_dropout(0, 2 * A, 3 * A, 4 * A, 5 * A, 1, 4, 2, 128, 128, 1, 0.1, 0.2, 7, None) == 1
+    assert lib.attn_fwd_dropout(A, 2 * A, 3 * A, 4 * A, 5 * A, 1, 4, 3, 128, 128, 1, 0.1, 0.2, 7, None) == 2
+    assert lib.attn_fwd_dropout(A, 2 * A, 3 * A, A, 5 * A, 1, 4, 2, 128, 128, 1, 0.1, 0.2, 7, None) == 9

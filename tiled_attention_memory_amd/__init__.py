@@ -1,6 +1,7 @@
 """Exact causal GQA attention for MI355X (gfx950): HIP kernels behind a C ABI.
 
-The Python names mirror include/attn.h, include/attn_block.h and include/attn_decode.h. The library is loaded on first use
+The Python names mirror include/attn.h, include/attn_block.h, include/attn_decode.h and
+include/attn_dropout.h. The library is loaded on first use
 and every call fails loudly if it is missing; nothing here computes attention.
 """
 from ._binding import (  # noqa: F401
@@ -17,6 +18,8 @@ from ._binding import (  # noqa: F401
     attn_bwd_block_workspace_bytes,
     attn_decode,
     attn_decode_workspace_bytes,
+    attn_bwd_dropout,
+    attn_fwd_dropout,
     attn_fwd_block,
     attn_merge,
     attn_bwd,

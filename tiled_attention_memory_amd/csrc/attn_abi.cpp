@@ -1,9 +1,10 @@
 // C ABI of libattn.so: argument validation, then dispatch to the kernels.
 // The contract (layout, ownership, error behaviour) is stated in include/attn.h
-// include/attn_block.h and include/attn_decode.h.
+// include/attn_block.h, include/attn_decode.h and include/attn_dropout.h.
 #include "attn.h"
 #include "attn_block.h"
 #include "attn_decode.h"
+#include "attn_dropout.h"
 
 #include <math.h>
 #include <stdint.h>
@@ -82,8 +83,16 @@ extern "C" {
 
 #define ATTN_EXPORT __attribute__((visibility("default")))
 
-ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-             int S, int D, int causal, float scale, hipStream_t stream) {
+namespace {
+// Dropout threshold of probability p (see attn_dropout.h), or -1 when p is out of range.
+int drop_threshold(float p) {
+  if (!isfinite(p) || p < 0.f) return -1;
+  const double t = floor(256.0 * (double)p + 0.5);
+  return t > 255.0 ? -1 : (int)t;
+}
+
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int S, int D,
+               int causal, float scale, int drop_t, unsigned long long seed, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_POINTER;
   int st = check_common(B, Hq, Hkv, S, S, D, causal, scale);
   if (st != ATTN_OK) return st;
@@ -97,13 +106,29 @@ ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, f
       overlap(rl, rv) || overlap(ro, rl))
     return ATTN_ERR_ALIAS;
   try {
-    const tam::AttnShape sh = square_shape(B, Hq, Hkv, S, D, causal, scale);
+    tam::AttnShape sh = square_shape(B, Hq, Hkv, S, D, causal, scale);
+    sh.drop_t = drop_t;
+    sh.seed = seed;
     return from_hip(tam::launch_fwd(sh, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), nullptr, lse,
                                     stream));
   } catch (...) {
     return ATTN_ERR_HIP;
   }
+}
+}  // namespace
+
+ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+             int S, int D, int causal, float scale, hipStream_t stream) {
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, S, D, causal, scale, 0, 0, stream);
+}
+
+ATTN_EXPORT int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                                 int Hkv, int S, int D, int causal, float scale, float p, unsigned long long seed,
+                                 hipStream_t stream) {
+  const int t = drop_threshold(p);
+  if (t < 0) return ATTN_ERR_BAD_SCALE;
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, S, D, causal, scale, t, seed, stream);
 }
 
 ATTN_EXPORT int attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes) {
@@ -114,17 +139,20 @@ ATTN_EXPORT int attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, s
   return ATTN_OK;
 }
 
-ATTN_EXPORT int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                               const float* lse, void* dq, void* dk, void* dv, void* workspace,
-                               size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int causal,
-                               float scale, hipStream_t stream, hipEvent_t* events) {
+namespace {
+int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+               void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D,
+               int causal, float scale, int drop_t, unsigned long long seed, hipStream_t stream,
+               hipEvent_t* events) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL_POINTER;
   int st = check_common(B, Hq, Hkv, S, S, D, causal, scale);
   if (st != ATTN_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return ATTN_ERR_MISALIGNED;
-  const tam::AttnShape sh = square_shape(B, Hq, Hkv, S, D, causal, scale);
+  tam::AttnShape sh = square_shape(B, Hq, Hkv, S, D, causal, scale);
+  sh.drop_t = drop_t;
+  sh.seed = seed;
   const size_t need = tam::bwd_workspace_bytes(sh);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_MISALIGNED;
@@ -148,6 +176,26 @@ ATTN_EXPORT int attn_bwd_timed(const void* q, const void* k, const void* v, cons
   } catch (...) {
     return ATTN_ERR_HIP;
   }
+}
+
+}  // namespace
+
+ATTN_EXPORT int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                               size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int causal,
+                               float scale, hipStream_t stream, hipEvent_t* events) {
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, S, D, causal, scale,
+                    0, 0, stream, events);
+}
+
+ATTN_EXPORT int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                 const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                                 size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int causal,
+                                 float scale, float p, unsigned long long seed, hipStream_t stream) {
+  const int t = drop_threshold(p);
+  if (t < 0) return ATTN_ERR_BAD_SCALE;
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, S, D, causal, scale,
+                    t, seed, stream, nullptr);
 }
 
 ATTN_EXPORT int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

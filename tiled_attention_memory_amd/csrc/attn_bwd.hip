@@ -141,6 +141,7 @@ struct DkdvArgs {
   int Hq, Hkv, Sq, Sk, dlt, nsplit;
   float c;      // scale * log2(e)
   float scale;
+  DropParams drop;  // dropout on the probabilities (DROP kernels only)
   TileSched sched;  // streams = (batch*Hkv + kv head) * nsplit + subset; tiles = key tiles
 };
 
@@ -158,7 +159,7 @@ struct DkdvLayout {
   static constexpr int BYTES = PB + 4 * PB_BLOCK;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(DkdvArgs a) {
   using T = SwzTile<D>;
@@ -263,7 +264,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   // before the wave's keys are skipped. The P role computes S and P, hands P to
   // its partner and accumulates dV; the dS role computes dP, takes P, forms dS
   // and accumulates dK. The barrier in the middle orders the hand-off.
-  auto tile = [&](auto masked_tag, auto stage_tag, int it) TAM_INLINE {
+  auto tile = [&](auto masked_tag, auto stage_tag, int it, uint32_t bhq) TAM_INLINE {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int STG = decltype(stage_tag)::value;
     constexpr int QB = STG ? L::Q1 : L::Q0, DOB = STG ? L::DO1 : L::DO0, FB = STG ? L::F1 : L::F0;
@@ -292,6 +293,11 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const f32x4 l2 = *reinterpret_cast<const f32x4*>(Fs + qs * 32 + 8 * i + 4 * half);
+          // dropout bytes of rows R .. R + 3 (word r) for this lane's key (byte kvrow % 4)
+          u32x4 dw = {0u, 0u, 0u, 0u};
+          if (DROP)
+            dw = philox4x32_10((uint32_t)kvrow >> 2, (uint32_t)(it * kKBR + qs * 32 + 8 * i + 4 * half) >> 2, bhq,
+                               0u, a.drop.seed_lo, a.drop.seed_hi);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int v = 4 * i + r;
@@ -301,8 +307,16 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
               const bool ok = run[qs] && qrow < Sq && kvrow < Sk && (!CAUSAL || kvrow <= qrow + dlt);
               e = ok ? e : 0.f;
             }
-            p[v] = e;
-            pbuf[(16 * qs + v) * 64] = e;
+            if (DROP) {
+              // P goes to the partner with the sign carrying the mask; dV uses
+              // the kept probabilities scaled by r
+              const bool keep = drop_keep(dw[r], kvrow & 3, a.drop.t);
+              pbuf[(16 * qs + v) * 64] = keep ? e : -e;
+              p[v] = keep ? e * a.drop.r : 0.f;
+            } else {
+              p[v] = e;
+              pbuf[(16 * qs + v) * 64] = e;
+            }
           }
         }
 #pragma unroll
@@ -320,7 +334,9 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int v = 4 * i + r;
-            ds[v] = pbuf[(16 * qs + v) * 64] * (x[qs][v] - dl4[r]);
+            const float pv = pbuf[(16 * qs + v) * 64];
+            ds[v] = DROP ? fabsf(pv) * ((__builtin_signbit(pv) ? 0.f : a.drop.r) * x[qs][v] - dl4[r])
+                         : pv * (x[qs][v] - dl4[r]);
           }
         }
 #pragma unroll
@@ -353,10 +369,11 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
     // the whole workgroup takes the same branch: the tile meets the diagonal of
     // the unit's 128 keys, or the end of the sequence
     const bool masked = (CAUSAL && it * kKBR + dlt < kvt0 + kKBC) || it * kKBR + kKBR > Sq || kvt0 + kKBC > Sk;
+    const uint32_t bhq = (uint32_t)(b * a.Hq + step_head(st));
     if (masked)
-      tile(std::true_type{}, stage_tag, it);
+      tile(std::true_type{}, stage_tag, it, bhq);
     else
-      tile(std::false_type{}, stage_tag, it);
+      tile(std::false_type{}, stage_tag, it, bhq);
     wait_loads();
     __syncthreads();
   };
@@ -440,6 +457,7 @@ struct DqArgs {
   int Hq, Hkv, Sq, Sk, dlt;
   float c;
   float scale;
+  DropParams drop;  // dropout on the probabilities (DROP kernels only)
   TileSched sched;
 };
 
@@ -455,7 +473,7 @@ struct DqLayout {
   static_assert(4 * (D / 32) * 16 * 64 * 4 <= PB, "final hand-off fits in the stages");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(DqArgs a) {
   using T = SwzTile<D>;
@@ -572,6 +590,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float pf[16];
+        uint32_t dbytes = 0u;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           float e = fast_exp2(fmaf(x[kb][v], c, -rowval));
@@ -581,7 +600,15 @@ void attn_bwd_dq_kernel(DqArgs a) {
             e = ok ? e : 0.f;
           }
           pf[v] = e;
-          pbuf[(16 * kb + v) * 64] = e;
+          if (DROP) {
+            // P K uses P before dropout; the partner gets P with the sign carrying the mask
+            if ((v & 3) == 0)
+              dbytes = drop_row_bytes(a.drop, (uint32_t)bh, (uint32_t)qrow,
+                                      (uint32_t)(kv0 + kb * 32 + 8 * (v >> 2) + 4 * half) >> 2);
+            pbuf[(16 * kb + v) * 64] = drop_keep(dbytes, v & 3, a.drop.t) ? e : -e;
+          } else {
+            pbuf[(16 * kb + v) * 64] = e;
+          }
         }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) ph[kb][k2] = pack_bf16x8(pf + 8 * k2);
@@ -614,7 +641,9 @@ void attn_bwd_dq_kernel(DqArgs a) {
       float ds[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        ds[v] = pbuf[(16 * kb + v) * 64] * (x[kb][v] - rowval);
+        const float pv = pbuf[(16 * kb + v) * 64];
+        ds[v] = DROP ? fabsf(pv) * ((__builtin_signbit(pv) ? 0.f : a.drop.r) * x[kb][v] - rowval)
+                     : pv * (x[kb][v] - rowval);
         csum += ds[v];
       }
       bf16x8 dh[2], dl[2];
@@ -807,12 +836,14 @@ hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, 
   a.dlt = sh.dlt;
   a.c = sh.scale * kLog2e;
   a.scale = sh.scale;
+  a.drop = make_drop(sh.drop_t, sh.seed);
   a.sched.BH = sh.B * sh.Hq;
   a.sched.NT = (sh.Sq + kQBR - 1) / kQBR;
   a.sched.chunk = (a.sched.BH + 7) / 8;
   void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL>),
-                         dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
+  const void* kern = a.drop.t ? reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, true>)
+                              : reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, false>);
+  return hipLaunchKernel(kern, dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -836,12 +867,14 @@ hipError_t launch_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k
   a.nsplit = ws.w.nsplit;
   a.c = sh.scale * kLog2e;
   a.scale = sh.scale;
+  a.drop = make_drop(sh.drop_t, sh.seed);
   a.sched.BH = sh.B * sh.Hkv * ws.w.nsplit;
   a.sched.NT = (sh.Sk + kKBC - 1) / kKBC;
   a.sched.chunk = (a.sched.BH + 7) / 8;
   void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL>),
-                         dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
+  const void* kern = a.drop.t ? reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, true>)
+                              : reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, false>);
+  return hipLaunchKernel(kern, dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
 }
 
 hipError_t launch_reduce(const AttnShape& sh, uint16_t* dk, uint16_t* dv, const Ws& ws, hipStream_t stream) {

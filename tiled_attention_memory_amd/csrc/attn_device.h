@@ -224,6 +224,64 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // Wait until this wave's outstanding global loads (including loads into LDS) are done.
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Dropout on the probabilities, with a keep mask regenerated from a
+// counter-based generator instead of stored: Philox4x32-10 (Salmon, Moraes,
+// Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011).
+// A round multiplies words 0 and 2 by two constants (64-bit products split
+// into high and low words) and mixes in the other two words and the key; the
+// key advances by two Weyl increments between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// One generator call covers a 4 x 4 block of (query row i, key j) of one
+// query head: counter (j / 4, i / 4, b * Hq + h, 0), key = the 64-bit seed;
+// the pair's byte is byte j % 4 (low byte first) of word i % 4, and the pair
+// is kept when that byte is at least t (dropout probability t / 256, kept
+// probabilities scaled by r = 256 / (256 - t)).
+struct DropParams {
+  uint32_t seed_lo, seed_hi;
+  uint32_t t;  // 0..255
+  float r;
+};
+
+__host__ inline DropParams make_drop(int t, unsigned long long seed) {
+  DropParams d;
+  d.seed_lo = (uint32_t)seed;
+  d.seed_hi = (uint32_t)(seed >> 32);
+  d.t = (uint32_t)t;
+  d.r = 256.f / (float)(256 - t);
+  return d;
+}
+
+// The 4 bytes of row i for keys 4 * k4 .. 4 * k4 + 3 (byte n for key 4 k4 + n).
+__device__ __forceinline__ uint32_t drop_row_bytes(const DropParams& d, uint32_t bhq, uint32_t i, uint32_t k4) {
+  const u32x4 w = philox4x32_10(k4, i >> 2, bhq, 0u, d.seed_lo, d.seed_hi);
+  const uint32_t s = i & 3u;
+  return s == 0 ? w[0] : s == 1 ? w[1] : s == 2 ? w[2] : w[3];
+}
+
+// Whether byte n (0..3) of a word of drop bytes keeps its pair.
+__device__ __forceinline__ bool drop_keep(uint32_t bytes, int n, uint32_t t) {
+  return ((bytes >> (8 * n)) & 0xFFu) >= t;
+}
+
 // Scheduler shared by the kernels: work unit = (stream, tile), a stream being
 // a query head or a (key/value head, head subset) pair. Workgroup i runs on
 // XCD i % 8. When the streams divide evenly over the 8 XCDs, XCD x owns a

@@ -54,6 +54,7 @@ struct FwdArgs {
   // lse + s * lse_stride.
   int pack, kv_chunk;
   long long o_stride, lse_stride;
+  DropParams drop;  // dropout on the probabilities (DROP kernels only)
   TileSched sched;
 };
 
@@ -63,7 +64,7 @@ struct FwdArgs {
 // skipped for most tiles.
 constexpr float kLazyMax = 8.f;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   using T = SwzTile<D>;
   constexpr int KS = D / 16;          // MFMA k-steps over the head dimension
@@ -246,6 +247,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         lsum += e;
       }
     l_run += lsum;
+    if (DROP) {
+      // the row sum above is taken before dropout; the product with V uses
+      // the kept probabilities scaled by r
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t k4 = (uint32_t)(kv0 + 32 * (KB0 + kb) + 8 * i + 4 * half) >> 2;
+          const uint32_t bytes = drop_row_bytes(a.drop, (uint32_t)bh, (uint32_t)tok, k4);
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            p[kb][4 * i + r4] = drop_keep(bytes, r4, a.drop.t) ? p[kb][4 * i + r4] * a.drop.r : 0.f;
+        }
+    }
 
     bf16x8 pb[NKB][2];
 #pragma unroll
@@ -381,14 +396,16 @@ hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, con
   a.pack = 0;
   a.kv_chunk = 0;
   a.o_stride = a.lse_stride = 0;
+  a.drop = make_drop(sh.drop_t, sh.seed);
   a.c = sh.scale * kLog2e;
   a.sched.BH = sh.B * sh.Hq;
   a.sched.NT = (sh.Sq + kBR - 1) / kBR;
   a.sched.chunk = (a.sched.BH + 7) / 8;
   const long long grid = sched_grid(a.sched);
   void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL>),
-                         dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+  const void* kern = a.drop.t ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL, true>)
+                              : reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL, false>);
+  return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -414,6 +431,7 @@ hipError_t launch_decode_t(const AttnShape& sh, const uint16_t* q, const uint16_
   a.kv_chunk = p.chunk;
   a.o_stride = rows * sh.D;
   a.lse_stride = rows;
+  a.drop = DropParams{0u, 0u, 0u, 1.f};
   a.c = sh.scale * kLog2e;
   a.sched.BH = sh.B * sh.Hkv;
   a.sched.NT = p.splits;

@@ -17,6 +17,10 @@ struct AttnShape {
   bool causal;
   int dlt;
   float scale;
+  // dropout on the probabilities: byte threshold t (probability t / 256; 0 =
+  // none) and the generator seed
+  int drop_t = 0;
+  unsigned long long seed = 0;
 };
 
 constexpr int kMaxMerge = 16;  // partial results one merge call combines
