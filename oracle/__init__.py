@@ -6,3 +6,4 @@ package. The HIP library neither imports it nor is imported by it.
 from . import attention  # noqa: F401
 from . import blocks  # noqa: F401
 from . import dropout  # noqa: F401
+from . import rope  # noqa: F401
