@@ -284,6 +284,9 @@ def main():
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
                     help="run the step with dropout probability P on the probabilities "
                          "(attn_fwd_dropout / attn_bwd_dropout); the headline runs without")
+    ap.add_argument("--rope", type=float, default=0.0, metavar="BASE",
+                    help="run the step with rotary position embedding of this base on Q and K "
+                         "(attn_fwd_rope / attn_bwd_rope); the headline runs without")
     ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
                     help="before each step, overwrite a MIB-mebibyte buffer so that L2 and the "
                          "memory-side cache start cold (for the short, bandwidth-bound shapes); "
@@ -321,25 +324,31 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = tam.workspace_for(q, k)
+    ws = tam.rope_workspace_for(q, k) if args.rope else tam.workspace_for(q, k)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
     def step(ev_f=None, ev_b=None):
         if ev_f:
             hip.record(ev_f[0], sh)
-        if args.dropout:
+        if args.rope:
+            tam.attn_fwd_rope(q, k, v, o, lse, ws, args.rope, causal=True, scale=w.scale, stream=stream)
+        elif args.dropout:
             tam.attn_fwd_dropout(q, k, v, o, lse, args.dropout, 1234, causal=True, scale=w.scale, stream=stream)
         else:
             tam.attn_fwd(q, k, v, o, lse, causal=True, scale=w.scale, stream=stream)
         if ev_f:
             hip.record(ev_f[1], sh)
-        if args.dropout:
-            # no per-kernel events on this path: the whole backward pass is bracketed instead
+        if args.dropout or args.rope:
+            # no per-kernel events on these paths: the whole backward pass is bracketed instead
             if ev_b:
                 hip.record(ev_b[0], sh)
-            tam.attn_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, ws, args.dropout, 1234, causal=True,
-                                 scale=w.scale, stream=stream)
+            if args.rope:
+                tam.attn_bwd_rope(q, k, v, o, do, lse, dq, dk, dv, ws, args.rope, causal=True, scale=w.scale,
+                                  stream=stream)
+            else:
+                tam.attn_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, ws, args.dropout, 1234, causal=True,
+                                     scale=w.scale, stream=stream)
             if ev_b:
                 for i in range(1, tam.BWD_EVENTS):
                     hip.record(ev_b[i], sh)
@@ -436,9 +445,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name + (f"_dropout{args.dropout:g}" if args.dropout else ""), "B": w.B,
+        "config": {"workload": w.name + (f"_dropout{args.dropout:g}" if args.dropout else "")
+                   + (f"_rope{args.rope:g}" if args.rope else ""), "B": w.B,
                    "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D, "causal": True, "global_batch": w.B,
-                   "seq_len": w.S, "parallelism": "none", **({"dropout": args.dropout} if args.dropout else {})},
+                   "seq_len": w.S, "parallelism": "none", **({"dropout": args.dropout} if args.dropout else {}),
+                   **({"rope_base": args.rope} if args.rope else {})},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(w.fwd_flops() / (per["attn_fwd_kernel"] * 1e-3) / 1e12, 1),
         "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),

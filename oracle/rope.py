@@ -20,6 +20,12 @@ linear, the gradients with respect to the unrotated inputs are R_m^T applied
 to the gradients with respect to Q' and K' (the inverse rotation).
 Row i of the sequence sits at position i. (A common offset of all positions
 would change nothing: the scores depend on position differences only.)
+
+Precision. The attention inputs are bf16 tensors, and so are the rotated Q
+and K that feed the products when the rotation runs ahead of them (as its own
+step on bf16 tensors, or fused into the load of the attention kernel): by
+default the rotated values are rounded to bf16, nearest with ties to even,
+and the gradient treats that rounding as the identity.
 """
 from __future__ import annotations
 
@@ -45,7 +51,14 @@ def rotate(x, positions, base, inverse=False):
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
 
 
-def backward(q, k, v, do, scale, causal, base):
+def round_bf16(x):
+    """Nearest bfloat16 value (8 significant bits, ties to even) of float64 values."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                    # x = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def backward(q, k, v, do, scale, causal, base, bf16_rotated=True):
     """Forward and backward of attention on RoPE-rotated Q and K ([B, H, S, D] float64).
 
     Returns o, lse and the gradients with respect to the unrotated q, k and v.
@@ -53,6 +66,8 @@ def backward(q, k, v, do, scale, causal, base):
     S = q.shape[2]
     pos = np.arange(S)
     qr, kr = rotate(q, pos, base), rotate(k, pos, base)
+    if bf16_rotated:
+        qr, kr = round_bf16(qr), round_bf16(kr)
     r = att.backward(qr, kr, v, do, scale, causal=causal)
     return {"o": r["o"], "lse": r["lse"], "dq": rotate(r["dq"], pos, base, inverse=True),
             "dk": rotate(r["dk"], pos, base, inverse=True), "dv": r["dv"], "q_rot": qr, "k_rot": kr}

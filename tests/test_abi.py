@@ -1,5 +1,6 @@
 """C ABI contract on the CPU: the library loads, exports what include/attn.h and
-include/attn_block.h, include/attn_decode.h and include/attn_dropout.h declare, and rejects every invalid argument before
+include/attn_block.h, include/attn_decode.h, include/attn_dropout.h and include/attn_rope.h
+declare, and rejects every invalid argument before
 touching the GPU.
 
 Every call below fails validation, and validation happens before any HIP
@@ -14,7 +15,8 @@ import pytest
 import tiled_attention_memory_amd as tam
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("attn.h", "attn_block.h", "attn_decode.h", "attn_dropout.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("attn.h", "attn_block.h", "attn_decode.h", "attn_dropout.h",
+                                                         "attn_rope.h")]
 
 A = 1 << 20          # fake, 16-byte aligned, far-apart "device" addresses (never dereferenced)
 GOOD = dict(B=1, Hq=4, Hkv=2, S=128, D=128, causal=1, scale=0.125)
@@ -245,3 +247,23 @@ def test_dropout_other_errors_match_attn_fwd():
     assert lib.attn_fwd_dropout(0, 2 * A, 3 * A, 4 * A, 5 * A, 1, 4, 2, 128, 128, 1, 0.1, 0.2, 7, None) == 1
     assert lib.attn_fwd_dropout(A, 2 * A, 3 * A, 4 * A, 5 * A, 1, 4, 3, 128, 128, 1, 0.1, 0.2, 7, None) == 2
     assert lib.attn_fwd_dropout(A, 2 * A, 3 * A, A, 5 * A, 1, 4, 2, 128, 128, 1, 0.1, 0.2, 7, None) == 9
+
+
+# ---------------------------------------------------------------------------
+# rotary embedding (attn_rope.h): validation only
+# ---------------------------------------------------------------------------
+def test_rope_rejects():
+    lib = tam.load()
+    B, Hq, Hkv, S, D = 1, 4, 2, 128, 128
+    need = tam.attn_rope_workspace_bytes(B, Hq, Hkv, S, D)
+    assert need > tam.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)
+    W = 64 * A
+    for base in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.attn_fwd_rope(A, 2 * A, 3 * A, 4 * A, 5 * A, W, need, B, Hq, Hkv, S, D, 1, 0.1, base, None) == 4
+        assert lib.attn_bwd_rope(A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, 8 * A, 9 * A, W, need, B, Hq, Hkv, S, D,
+                                 1, 0.1, base, None) == 4
+    assert lib.attn_fwd_rope(A, 2 * A, 3 * A, 4 * A, 5 * A, W, need - 1, B, Hq, Hkv, S, D, 1, 0.1, 1e4, None) == 6
+    assert lib.attn_fwd_rope(A, 2 * A, 3 * A, 4 * A, 5 * A, A + 128, need, B, Hq, Hkv, S, D, 1, 0.1, 1e4, None) == 9
+    assert lib.attn_bwd_rope(A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, 8 * A, 9 * A, W, 16, B, Hq, Hkv, S, D, 1, 0.1,
+                             1e4, None) == 6
+    assert lib.attn_fwd_rope(A, 2 * A, 3 * A, 4 * A, 5 * A, W, need, B, Hq, Hkv, S, 96, 1, 0.1, 1e4, None) == 3

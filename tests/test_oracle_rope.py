@@ -42,7 +42,7 @@ def pin_gradients_against_torch(mod):
     B, hq, hkv, S, D = 1, 4, 2, 11, 8
     q, k, v, do = rand((B, hq, S, D), 94), rand((B, hkv, S, D), 95), rand((B, hkv, S, D), 96), rand((B, hq, S, D), 97)
     base = 1e4
-    r = mod.backward(q, k, v, do, 0.4, True, base)
+    r = mod.backward(q, k, v, do, 0.4, True, base, bf16_rotated=False)
     tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
     pos = torch.arange(S, dtype=torch.float64)
     inv = base ** (-2.0 * torch.arange(D // 2, dtype=torch.float64) / D)
@@ -60,7 +60,21 @@ def pin_gradients_against_torch(mod):
             and close(r["dk"], tk.grad.numpy(), 1e-11) and close(r["dv"], tv.grad.numpy(), 1e-11))
 
 
-ALL = [pin_closed_forms, pin_relative_positions, pin_gradients_against_torch]
+def pin_round_bf16(mod):
+    """Ties go to the even neighbour, other values to the nearest one (spacing 2^-7 on [1, 2));
+    agrees with rounding the float32 bit pattern on values that are exact in float32."""
+    r = mod.round_bf16
+    ok = r(1 + 2.0 ** -8) == 1.0 and r(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+    ok &= r(1 + 2.0 ** -8 + 2.0 ** -20) == 1 + 2.0 ** -7 and r(-(1 + 3 * 2.0 ** -8)) == -(1 + 2.0 ** -6)
+    ok &= r(0.0) == 0.0 and r(3.0) == 3.0 and r(2.0 ** -130) == 2.0 ** -130
+    x = rand((4096,), 98).astype(np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    ok &= bool(np.array_equal(r(x.astype(np.float64)), bits.astype(np.uint32).view(np.float32).astype(np.float64)))
+    return ok
+
+
+ALL = [pin_closed_forms, pin_relative_positions, pin_gradients_against_torch, pin_round_bf16]
 
 
 @pytest.mark.parametrize("pin", ALL, ids=lambda p: p.__name__)
@@ -74,6 +88,7 @@ MUTATIONS = {
     "sign_of_sine": ("[lo * c - hi * s, hi * c + lo * s]", "[lo * c + hi * s, hi * c - lo * s]"),
     "frequency_exponent": ("-2.0 * d / D", "-d / D"),
     "gradient_not_rotated_back": ('"dq": rotate(r["dq"], pos, base, inverse=True)', '"dq": r["dq"]'),
+    "round_ties_up": ("np.rint(m * 256.0)", "np.floor(m * 256.0 + 0.5)"),
     "key_positions_reversed": ("qr, kr = rotate(q, pos, base), rotate(k, pos, base)",
                                "qr, kr = rotate(q, pos, base), rotate(k, pos[::-1], base)"),
 }

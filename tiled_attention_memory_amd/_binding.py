@@ -1,8 +1,8 @@
 """ctypes binding of libattn.so: argument marshalling only.
 
 Every computation happens in the HIP kernels behind the C ABI declared in
-include/attn.h, include/attn_block.h, include/attn_decode.h and
-include/attn_dropout.h. PyTorch is used only to own device memory and to provide the
+include/attn.h, include/attn_block.h, include/attn_decode.h,
+include/attn_dropout.h and include/attn_rope.h. PyTorch is used only to own device memory and to provide the
 stream handle. There is no fallback: if the library is missing, every call
 raises.
 """
@@ -25,7 +25,8 @@ STATUS = {
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_bwd_workspace_bytes", "attn_status_string",
            "attn_version", "attn_fwd_block", "attn_merge", "attn_bwd_block_workspace_bytes",
            "attn_bwd_block_begin", "attn_bwd_block_dq", "attn_bwd_block_dq_end", "attn_bwd_block_dkdv",
-           "attn_decode_workspace_bytes", "attn_decode", "attn_fwd_dropout", "attn_bwd_dropout")
+           "attn_decode_workspace_bytes", "attn_decode", "attn_fwd_dropout", "attn_bwd_dropout",
+           "attn_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope")
 BWD_EVENTS = 5
 MAX_MERGE = 16
 
@@ -77,9 +78,13 @@ def load() -> ctypes.CDLL:
         ull = ctypes.c_ulonglong
         lib.attn_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, ull, vp]
         lib.attn_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, f, ull, vp]
+        lib.attn_rope_workspace_bytes.argtypes = [i, i, i, i, i, ctypes.POINTER(sz)]
+        lib.attn_fwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, f, vp]
+        lib.attn_bwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, f, vp]
         for name in ("attn_fwd_block", "attn_merge", "attn_bwd_block_workspace_bytes", "attn_bwd_block_begin",
                      "attn_bwd_block_dq", "attn_bwd_block_dq_end", "attn_bwd_block_dkdv",
-                     "attn_decode_workspace_bytes", "attn_decode", "attn_fwd_dropout", "attn_bwd_dropout"):
+                     "attn_decode_workspace_bytes", "attn_decode", "attn_fwd_dropout", "attn_bwd_dropout",
+           "attn_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope"):
             getattr(lib, name).restype = i
         _lib = lib
         return lib
@@ -368,3 +373,42 @@ def attn_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace, p, seed, caus
     _raise(load().attn_bwd_dropout(*ptrs, *_ws_ptr(workspace), B, Hq, Hkv, S, D, int(bool(causal)),
                                    _scale(scale, D), float(p), int(seed) & 0xFFFFFFFFFFFFFFFF, _stream(stream)),
            "attn_bwd_dropout")
+
+
+# ---------------------------------------------------------------------------
+# rotary position embedding (include/attn_rope.h)
+# ---------------------------------------------------------------------------
+def attn_rope_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, D: int) -> int:
+    out = ctypes.c_size_t(0)
+    _raise(load().attn_rope_workspace_bytes(B, Hq, Hkv, S, D, ctypes.byref(out)), "attn_rope_workspace_bytes")
+    return out.value
+
+
+def rope_workspace_for(q, k):
+    import torch
+    B, Hq, Hkv, S, D = _shape(q, k)
+    return torch.empty(attn_rope_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8, device=q.device)
+
+
+def attn_fwd_rope(q, k, v, o, lse, workspace, base, causal=True, scale=None, stream=None) -> None:
+    import torch
+    B, Hq, Hkv, S, D = _shape(q, k)
+    bf = torch.bfloat16
+    ptrs = [_check(q, "q", bf, (B, Hq, S, D)), _check(k, "k", bf, (B, Hkv, S, D)),
+            _check(v, "v", bf, (B, Hkv, S, D)), _check(o, "o", bf, (B, Hq, S, D)),
+            _check(lse, "lse", torch.float32, (B, Hq, S))]
+    _raise(load().attn_fwd_rope(*ptrs, *_ws_ptr(workspace), B, Hq, Hkv, S, D, int(bool(causal)), _scale(scale, D),
+                                float(base), _stream(stream)), "attn_fwd_rope")
+
+
+def attn_bwd_rope(q, k, v, o, dout, lse, dq, dk, dv, workspace, base, causal=True, scale=None, stream=None) -> None:
+    import torch
+    B, Hq, Hkv, S, D = _shape(q, k)
+    bf = torch.bfloat16
+    ptrs = [_check(q, "q", bf, (B, Hq, S, D)), _check(k, "k", bf, (B, Hkv, S, D)),
+            _check(v, "v", bf, (B, Hkv, S, D)), _check(o, "o", bf, (B, Hq, S, D)),
+            _check(dout, "dout", bf, (B, Hq, S, D)), _check(lse, "lse", torch.float32, (B, Hq, S)),
+            _check(dq, "dq", bf, (B, Hq, S, D)), _check(dk, "dk", bf, (B, Hkv, S, D)),
+            _check(dv, "dv", bf, (B, Hkv, S, D))]
+    _raise(load().attn_bwd_rope(*ptrs, *_ws_ptr(workspace), B, Hq, Hkv, S, D, int(bool(causal)), _scale(scale, D),
+                                float(base), _stream(stream)), "attn_bwd_rope")

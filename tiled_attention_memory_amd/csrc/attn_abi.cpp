@@ -1,10 +1,12 @@
 // C ABI of libattn.so: argument validation, then dispatch to the kernels.
 // The contract (layout, ownership, error behaviour) is stated in include/attn.h
-// include/attn_block.h, include/attn_decode.h and include/attn_dropout.h.
+// include/attn_block.h, include/attn_decode.h, include/attn_dropout.h and
+// include/attn_rope.h.
 #include "attn.h"
 #include "attn_block.h"
 #include "attn_decode.h"
 #include "attn_dropout.h"
+#include "attn_rope.h"
 
 #include <math.h>
 #include <stdint.h>
@@ -422,6 +424,84 @@ ATTN_EXPORT int attn_decode(const void* q, const void* k, const void* v, void* o
     return from_hip(tam::launch_decode(sh, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, workspace,
                                        stream));
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rotary position embedding (attn_rope.h)
+// ---------------------------------------------------------------------------
+ATTN_EXPORT int attn_rope_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes) {
+  if (!bytes) return ATTN_ERR_NULL_POINTER;
+  const int st = check_shape(B, Hq, Hkv, S, S, D);
+  if (st != ATTN_OK) return st;
+  *bytes = tam::rope_layout(square_shape(B, Hq, Hkv, S, D, 1, 1.f)).total;
+  return ATTN_OK;
+}
+
+ATTN_EXPORT int attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                              size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int causal, float scale,
+                              float base, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_POINTER;
+  int st = check_common(B, Hq, Hkv, S, S, D, causal, scale);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(base) || !(base > 0.f)) return ATTN_ERR_BAD_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_MISALIGNED;
+  const tam::AttnShape sh = square_shape(B, Hq, Hkv, S, D, causal, scale);
+  const size_t need = tam::rope_layout(sh).total;
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_MISALIGNED;
+  const size_t qb = (size_t)B * Hq * S * D * 2, kb = (size_t)B * Hkv * S * D * 2, lb = (size_t)B * Hq * S * 4;
+  const Range ins[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
+  const Range outs[] = {range_of(o, qb), range_of(lse, lb), range_of(workspace, need)};
+  for (int i = 0; i < 3; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return ATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return ATTN_ERR_ALIAS;
+  }
+  try {
+    return from_hip(tam::launch_fwd_rope(sh, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                         static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, workspace,
+                                         (double)base, stream));
+  } catch (...) {
+    return ATTN_ERR_HIP;
+  }
+}
+
+ATTN_EXPORT int attn_bwd_rope(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                              int B, int Hq, int Hkv, int S, int D, int causal, float scale, float base,
+                              hipStream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL_POINTER;
+  int st = check_common(B, Hq, Hkv, S, S, D, causal, scale);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(base) || !(base > 0.f)) return ATTN_ERR_BAD_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return ATTN_ERR_MISALIGNED;
+  const tam::AttnShape sh = square_shape(B, Hq, Hkv, S, D, causal, scale);
+  const size_t need = tam::rope_layout(sh).total;
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_MISALIGNED;
+  const size_t qb = (size_t)B * Hq * S * D * 2, kb = (size_t)B * Hkv * S * D * 2, lb = (size_t)B * Hq * S * 4;
+  const Range ins[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb), range_of(o, qb),
+                       range_of(dout, qb), range_of(lse, lb)};
+  const Range outs[] = {range_of(dq, qb), range_of(dk, kb), range_of(dv, kb), range_of(workspace, need)};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return ATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return ATTN_ERR_ALIAS;
+  }
+  try {
+    return from_hip(tam::launch_bwd_rope(sh, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                         static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
+                                         static_cast<const uint16_t*>(dout), lse, static_cast<uint16_t*>(dq),
+                                         static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), workspace,
+                                         (double)base, stream));
   } catch (...) {
     return ATTN_ERR_HIP;
   }

@@ -142,6 +142,7 @@ struct DkdvArgs {
   float c;      // scale * log2(e)
   float scale;
   DropParams drop;  // dropout on the probabilities (DROP kernels only)
+  const float2* rope_inv;  // (cos, sin) table [Sk][D/2]: rotate dK back; null = none
   TileSched sched;  // streams = (batch*Hkv + kv head) * nsplit + subset; tiles = key tiles
 };
 
@@ -389,6 +390,23 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   // lane holds key kvrow, head-dim entries 32db + 8i + 4half + (0..3)
   if (kvrow < Sk) {
     const float mul = vrole ? 1.f : a.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= mul;
+    if (!vrole && a.rope_inv) {
+      // dK of the rotated keys back to the unrotated ones: element v of
+      // block db is column 32db + 8(v/4) + 4half + v%4, its partner d + D/2
+      // sits in block db + DB/2 of this lane
+      const float2* cs = a.rope_inv + (size_t)kvrow * (D / 2);
+#pragma unroll
+      for (int db = 0; db < DB / 2; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float lo, hi;
+          rope_pair(acc[db][v], acc[db + DB / 2][v], cs[32 * db + 8 * (v >> 2) + 4 * half + (v & 3)], true, &lo, &hi);
+          acc[db][v] = lo;
+          acc[db + DB / 2][v] = hi;
+        }
+    }
     if (a.nsplit == 1) {
       uint16_t* op = (vrole ? a.dv : a.dk) + kv_base + (size_t)kvrow * D + 8 * half;
 #pragma unroll
@@ -400,7 +418,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const int i = 2 * m + t;
-            w[t] = u32x2{pack_bf16(A[4 * i] * mul, A[4 * i + 1] * mul), pack_bf16(A[4 * i + 2] * mul, A[4 * i + 3] * mul)};
+            w[t] = u32x2{pack_bf16(A[4 * i], A[4 * i + 1]), pack_bf16(A[4 * i + 2], A[4 * i + 3])};
           }
           *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
         }
@@ -412,8 +430,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const f32x16& A = acc[db];
-          f32x4 w = {A[4 * i] * mul, A[4 * i + 1] * mul, A[4 * i + 2] * mul, A[4 * i + 3] * mul};
-          *reinterpret_cast<f32x4*>(op + 32 * db + 8 * i) = w;
+          *reinterpret_cast<f32x4*>(op + 32 * db + 8 * i) = f32x4{A[4 * i], A[4 * i + 1], A[4 * i + 2], A[4 * i + 3]};
         }
     }
   }
@@ -458,6 +475,7 @@ struct DqArgs {
   float c;
   float scale;
   DropParams drop;  // dropout on the probabilities (DROP kernels only)
+  const float2* rope_inv;  // (cos, sin) table [Sq][D/2]: rotate dQ back (final mode); null = none
   TileSched sched;
 };
 
@@ -719,6 +737,26 @@ void attn_bwd_dq_kernel(DqArgs a) {
   if (prole) return;
   const float corr = sum_halves(csum);  // Delta_i - Delta~_i
   if (qrow < Sq) {
+    // dQ = scale (sum dS~ K - c P K); element v of block db is column
+    // 32db + 8(v/4) + 4half + v%4
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[db][v] = a.scale * fmaf(-corr, hand[(16 * db + v) * 64], acc[db][v]);
+    if (a.rope_inv) {
+      // back to the unrotated queries: the partner d + D/2 of column d sits in
+      // block db + DB/2 of this lane
+      const float2* cs = a.rope_inv + (size_t)qrow * (D / 2);
+#pragma unroll
+      for (int db = 0; db < DB / 2; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float lo, hi;
+          rope_pair(acc[db][v], acc[db + DB / 2][v], cs[32 * db + 8 * (v >> 2) + 4 * half + (v & 3)], true, &lo, &hi);
+          acc[db][v] = lo;
+          acc[db + DB / 2][v] = hi;
+        }
+    }
     uint16_t* op = a.dq + q_base + (size_t)qrow * D + 8 * half;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -728,11 +766,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int i = 2 * m + t;
-          float gq[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            gq[r] = a.scale * fmaf(-corr, hand[(16 * db + 4 * i + r) * 64], acc[db][4 * i + r]);
-          w[t] = u32x2{pack_bf16(gq[0], gq[1]), pack_bf16(gq[2], gq[3])};
+          w[t] = u32x2{pack_bf16(acc[db][4 * i], acc[db][4 * i + 1]), pack_bf16(acc[db][4 * i + 2], acc[db][4 * i + 3])};
         }
         *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
       }
@@ -837,6 +871,7 @@ hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, 
   a.c = sh.scale * kLog2e;
   a.scale = sh.scale;
   a.drop = make_drop(sh.drop_t, sh.seed);
+  a.rope_inv = sh.rope;
   a.sched.BH = sh.B * sh.Hq;
   a.sched.NT = (sh.Sq + kQBR - 1) / kQBR;
   a.sched.chunk = (a.sched.BH + 7) / 8;
@@ -868,6 +903,7 @@ hipError_t launch_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k
   a.c = sh.scale * kLog2e;
   a.scale = sh.scale;
   a.drop = make_drop(sh.drop_t, sh.seed);
+  a.rope_inv = sh.rope;
   a.sched.BH = sh.B * sh.Hkv * ws.w.nsplit;
   a.sched.NT = (sh.Sk + kKBC - 1) / kKBC;
   a.sched.chunk = (a.sched.BH + 7) / 8;

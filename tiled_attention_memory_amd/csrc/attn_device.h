@@ -282,6 +282,17 @@ __device__ __forceinline__ bool drop_keep(uint32_t bytes, int n, uint32_t t) {
   return ((bytes >> (8 * n)) & 0xFFu) >= t;
 }
 
+// Rotary position embedding (rotate-half pairing): the pair (x_d, x_{d+D/2})
+// of a row at position m turns by a_d = m * base^(-2d/D). The table holds
+// (cos a_d, sin a_d) per position and d < D/2, computed from fp64 angles. One
+// helper serves every kernel so that a rotated value is bit-identical
+// wherever it is formed; inverse = 1 turns the other way (gradients).
+__device__ __forceinline__ void rope_pair(float lo, float hi, float2 cs, bool inverse, float* out_lo, float* out_hi) {
+  const float sn = inverse ? -cs.y : cs.y;
+  *out_lo = __builtin_fmaf(lo, cs.x, -(hi * sn));
+  *out_hi = __builtin_fmaf(hi, cs.x, lo * sn);
+}
+
 // Scheduler shared by the kernels: work unit = (stream, tile), a stream being
 // a query head or a (key/value head, head subset) pair. Workgroup i runs on
 // XCD i % 8. When the streams divide evenly over the 8 XCDs, XCD x owns a

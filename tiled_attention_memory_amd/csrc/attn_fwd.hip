@@ -55,6 +55,7 @@ struct FwdArgs {
   int pack, kv_chunk;
   long long o_stride, lse_stride;
   DropParams drop;  // dropout on the probabilities (DROP kernels only)
+  const float2* rope;  // (cos, sin) table [Sq][D/2]: rotate the Q rows at load; null = none
   TileSched sched;
 };
 
@@ -125,12 +126,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   {
     const uint16_t* qp = a.q + row_off + 8 * half;
     const uint32_t flip = a.c < 0.f ? 0x80008000u : 0u;
+    u32x4 w[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 w = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
-      w ^= flip;
-      qf[ks] = __builtin_bit_cast(bf16x8, w);
+    for (int ks = 0; ks < KS; ++ks) w[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+    if (a.rope && row_ok) {
+      // rotary embedding at load: this lane holds elements 16 ks + 8 half + t,
+      // and the partner of element d < D/2 (d + D/2) sits in chunk ks + KS/2
+      const float2* cs = a.rope + (size_t)tok * (D / 2);
+#pragma unroll
+      for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 16 * ks + 8 * half + 2 * j;
+          float l0, l1, h0, h1;
+          rope_pair(bf16_lo(w[ks][j]), bf16_lo(w[ks + KS / 2][j]), cs[d], false, &l0, &h0);
+          rope_pair(bf16_hi(w[ks][j]), bf16_hi(w[ks + KS / 2][j]), cs[d + 1], false, &l1, &h1);
+          w[ks][j] = pack_bf16(l0, l1);
+          w[ks + KS / 2][j] = pack_bf16(h0, h1);
+        }
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, w[ks] ^ flip);
   }
 
   // Per-lane LDS offsets, fixed for every tile: row reads of K (row col, chunk
@@ -397,6 +413,7 @@ hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, con
   a.kv_chunk = 0;
   a.o_stride = a.lse_stride = 0;
   a.drop = make_drop(sh.drop_t, sh.seed);
+  a.rope = sh.rope;
   a.c = sh.scale * kLog2e;
   a.sched.BH = sh.B * sh.Hq;
   a.sched.NT = (sh.Sq + kBR - 1) / kBR;
@@ -432,6 +449,7 @@ hipError_t launch_decode_t(const AttnShape& sh, const uint16_t* q, const uint16_
   a.o_stride = rows * sh.D;
   a.lse_stride = rows;
   a.drop = DropParams{0u, 0u, 0u, 1.f};
+  a.rope = nullptr;
   a.c = sh.scale * kLog2e;
   a.sched.BH = sh.B * sh.Hkv;
   a.sched.NT = p.splits;

@@ -21,6 +21,9 @@ struct AttnShape {
   // none) and the generator seed
   int drop_t = 0;
   unsigned long long seed = 0;
+  // rotary embedding: (cos, sin) table [S][D/2] in device memory; the forward
+  // kernel rotates Q with it at load, the backward kernels rotate dQ and dK back
+  const float2* rope = nullptr;
 };
 
 constexpr int kMaxMerge = 16;  // partial results one merge call combines
@@ -43,6 +46,17 @@ struct DecodePlan {
 };
 DecodePlan decode_plan(const AttnShape& sh);
 size_t decode_workspace_bytes(const AttnShape& sh);
+// Rotary embedding (whole sequences, positions 0 .. S-1).
+struct RopeLayout {
+  size_t table, k_rot, q_rot, bwd, total;
+};
+RopeLayout rope_layout(const AttnShape& sh);
+hipError_t launch_fwd_rope(AttnShape sh, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                           float* lse, void* workspace, double base, hipStream_t stream);
+hipError_t launch_bwd_rope(AttnShape sh, const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                           const uint16_t* dout, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                           void* workspace, double base, hipStream_t stream);
+
 hipError_t launch_decode(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                          float* lse, void* workspace, hipStream_t stream);
 
