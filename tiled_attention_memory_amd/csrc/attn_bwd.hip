@@ -23,8 +23,10 @@
 //             pair while 64-row Q/dO tiles stream through LDS. In each pair one
 //             wave keeps K and dV^T in registers and computes P, which it hands
 //             to its partner through LDS; the partner keeps V and dK^T, computes
-//             dP and dS. No atomics: each unit owns its output rows; with more
-//             than one head subset, fp32 partials go to the workspace.
+//             dP and dS, one tile behind, so that the two waves' vector work
+//             and matrix products overlap. No atomics: each unit owns its output
+//             rows; with more than one head subset, fp32 partials go to the
+//             workspace.
 //   4. reduce (only with several subsets): sums the partials in a fixed order.
 // The second operand of every gradient product (P for dV, dS for dK and dQ)
 // enters the bf16 MFMA as a hi + lo pair of bf16 values, so those products
@@ -146,18 +148,20 @@ struct DkdvArgs {
   TileSched sched;  // streams = (batch*Hkv + kv head) * nsplit + subset; tiles = key tiles
 };
 
-// LDS layout of the dK/dV kernel, one array: the two streamed Q/dO stages
-// first (every streamed-tile read is then a per-lane offset plus an immediate
-// below 64 KiB), their lse2/delta rows, and the probabilities one wave of each
-// pair hands to the other.
+// LDS layout of the dK/dV kernel, one array. The two waves of a pair work one
+// streamed tile apart (see the kernel), so Q is kept in three stages (step t in
+// stage t % 3), dO in two (t % 2), the lse2/delta rows in three, and the
+// probabilities one wave of each pair hands to the other in two.
 template <int D>
 struct DkdvLayout {
   using T = SwzTile<D>;
-  static constexpr int Q0 = 0, DO0 = T::BYTES, Q1 = 2 * T::BYTES, DO1 = 3 * T::BYTES;
-  static constexpr int F0 = 4 * T::BYTES, F1 = F0 + 2 * kKBR * 4;  // lse2[64], delta[64] per stage
-  static constexpr int PB = F1 + 2 * kKBR * 4;                       // P: 4 key blocks x 64 rows x 32 keys fp32
+  static constexpr int Q0 = 0, DO0 = 3 * T::BYTES;
+  static constexpr int F0 = 5 * T::BYTES;            // lse2[64], delta[64] per stage
+  static constexpr int F_STAGE = 2 * kKBR * 4;
+  static constexpr int PB = F0 + 3 * F_STAGE;         // P: 4 key blocks x 64 rows x 32 keys fp32 per stage
   static constexpr int PB_BLOCK = kKBR * 32 * 4;
-  static constexpr int BYTES = PB + 4 * PB_BLOCK;
+  static constexpr int PB_STAGE = 4 * PB_BLOCK;
+  static constexpr int BYTES = PB + 2 * PB_STAGE;
 };
 
 template <int D, bool CAUSAL, bool DROP = false>
@@ -169,6 +173,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   constexpr int DB = D / 32;
   constexpr int SLD = T::LOADS / 4;             // streamed Q/dO loads per wave per tile
   static_assert(kKBR == T::ROWS && kKBC == 2 * T::ROWS, "tile sizes");
+  static_assert(L::BYTES <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
 
   int stream, t;
@@ -203,19 +208,39 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
                           : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
 
-  // per-lane LDS offsets, fixed for the whole unit (see SwzTile)
+  // Per-lane LDS offsets (see SwzTile) into the stage this wave reads next: rr
+  // for the row-by-key products (Q for the P role, dO for the dS role), tt for
+  // the transposed reads (dO, resp. Q). They move to the next stage in place,
+  // by a uniform step, so that a runtime stage costs no registers.
   const int i16 = lane & 15;
   const int dsub = 16 * ((lane >> 4) & 1);
   int rr[KS], tt[DB][2];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) rr[ks] = T::chunk_off(col, 2 * ks + half);
+  for (int ks = 0; ks < KS; ++ks) rr[ks] = (vrole ? L::Q0 : L::DO0) + T::chunk_off(col, 2 * ks + half);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi)
-      tt[db][hi] = T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
-  // this lane's slots of the P hand-off block: element v of 32-row block qs at (16 qs + v) * 64 + lane
-  float* pbuf = reinterpret_cast<float*>(smem + L::PB + kblk * L::PB_BLOCK) + lane;
+      tt[db][hi] = (vrole ? L::DO0 : L::Q0) +
+                   T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
+  // stage step after step st: Q stages cycle through three, dO stages through two
+  auto q_next = [&](int st) TAM_INLINE { return st % 3 == 2 ? -2 * T::BYTES : T::BYTES; };
+  auto do_next = [&](int st) TAM_INLINE { return (st & 1) ? -T::BYTES : T::BYTES; };
+  auto move_rr = [&](int by) TAM_INLINE {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) rr[ks] += by;
+  };
+  auto move_tt = [&](int by) TAM_INLINE {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) tt[db][hi] += by;
+  };
+  auto f_at = [&](int st) TAM_INLINE { return L::F0 + (st % 3) * L::F_STAGE; };
+  // this lane's slots of the P hand-off block of stage 0: element v of 32-row
+  // block qs at (16 qs + v) * 64 + lane
+  float* const pbuf = reinterpret_cast<float*>(smem + L::PB + kblk * L::PB_BLOCK) + lane;
+  auto pb_at = [&](int st) TAM_INLINE { return pbuf + (st & 1) * (L::PB_STAGE / 4); };
 
   const int NQ = (Sq + kKBR - 1) / kKBR;
   // first query tile with a row that sees the unit's first key (row >= kvt0 - dlt)
@@ -223,34 +248,47 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   const int per_head = max(0, NQ - i_min);  // query tiles visited per head
   const int nsteps = per_head * hps;
 
-  // step -> (query head, query tile): tiles run from the last one down, the
-  // subset's heads innermost, so that the units resident at the same time
+  // Steps visit (query head, query tile) with tiles from the last one down and
+  // the subset's heads innermost, so that the units resident at the same time
   // (whatever their key tile) stream the same Q/dO tiles together and share
-  // them in L2.
-  auto step_head = [&](int st) TAM_INLINE { return h_first + st % hps; };
-  auto step_tile = [&](int st) TAM_INLINE { return NQ - 1 - st / hps; };
+  // them in L2. A cursor walks them without divisions.
+  struct Cursor {
+    int h, it;
+  };
+  auto advance = [&](Cursor& cu) TAM_INLINE {
+    if (++cu.h == h_first + hps) {
+      cu.h = h_first;
+      --cu.it;
+    }
+  };
+  // the whole workgroup takes the same branch: the tile meets the diagonal of
+  // the unit's 128 keys, or the end of the sequence
+  auto masked_at = [&](int it) TAM_INLINE {
+    return (CAUSAL && it * kKBR + dlt < kvt0 + kKBC) || it * kKBR + kKBR > Sq || kvt0 + kKBC > Sk;
+  };
 
   int sld[SLD];
 #pragma unroll
   for (int i = 0; i < SLD; ++i) sld[i] = T::load_src((wave * SLD + i) % T::LOADS, lane);
 
-  // Q, dO tiles and their lse2, delta rows straight into stage `stg`; rows past Sq read as zeros.
-  auto issue = [&](int st, int stg) TAM_INLINE {
-    const int hq = step_head(st), row0 = step_tile(st) * kKBR;
-    const size_t bh = (size_t)b * a.Hq + hq;
+  // Q, dO tiles and their lse2, delta rows of step st (at cursor cu) straight
+  // into its stages; rows past Sq read as zeros.
+  auto issue = [&](int st, const Cursor& cu) TAM_INLINE {
+    const int row0 = cu.it * kKBR;
+    const size_t bh = (size_t)b * a.Hq + cu.h;
     const int rows_left = Sq - row0;
     const __amdgpu_buffer_rsrc_t rqd = make_rsrc(a.q + (bh * Sq + row0) * D, rows_left * D * 2);
     const __amdgpu_buffer_rsrc_t rdd = make_rsrc(a.dout + (bh * Sq + row0) * D, rows_left * D * 2);
-    const uint32_t base = lds0 + (stg ? L::Q1 : L::Q0);
+    const uint32_t qb = lds0 + L::Q0 + (st % 3) * T::BYTES, dob = lds0 + L::DO0 + (st & 1) * T::BYTES;
 #pragma unroll
     for (int i = 0; i < SLD; ++i) {
       const int gi = wave * SLD + i, which = gi / T::LOADS, li = gi % T::LOADS;
-      dma16(which == 0 ? rqd : rdd, base + which * T::BYTES + li * 1024, sld[i]);
+      dma16(which == 0 ? rqd : rdd, (which == 0 ? qb : dob) + li * 1024, sld[i]);
     }
     if (wave < 2) {
       const float* src = wave == 0 ? a.lse2 : a.delta;
       const __amdgpu_buffer_rsrc_t rf = make_rsrc(src + bh * Sq + row0, rows_left * 4);
-      dma4(rf, lds0 + (stg ? L::F1 : L::F0) + wave * kKBR * 4, lane * 4);
+      dma4(rf, lds0 + f_at(st) + wave * kKBR * 4, lane * 4);
     }
   };
 
@@ -259,132 +297,180 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   const float c = a.c;
 
-  // One streamed tile of 64 query rows (two 32-row blocks) against this wave's
-  // 32 keys. MASKED: the tile meets the diagonal of the unit's keys or the end
-  // of the sequence; hidden (query, key) pairs get P = 0 and blocks entirely
-  // before the wave's keys are skipped. The P role computes S and P, hands P to
-  // its partner and accumulates dV; the dS role computes dP, takes P, forms dS
-  // and accumulates dK. The barrier in the middle orders the hand-off.
-  auto tile = [&](auto masked_tag, auto stage_tag, int it, uint32_t bhq) TAM_INLINE {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    constexpr int STG = decltype(stage_tag)::value;
-    constexpr int QB = STG ? L::Q1 : L::Q0, DOB = STG ? L::DO1 : L::DO0, FB = STG ? L::F1 : L::F0;
-    const float* Fs = reinterpret_cast<const float*>(smem + FB);
-    bool run[2];
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) run[qs] = !(MASKED && CAUSAL && it * kKBR + qs * 32 + 31 + dlt < kvb0);
-    // Products over the head dim: S = Q K^T (P role) or dP = dO V^T (dS role);
-    // lane holds key kvrow, rows it*64 + 32qs + 8(v/4) + 4half + v%4.
-    const int AB = vrole ? QB : DOB;
-    f32x16 x[2];
+  // 32-row blocks of a streamed tile that hold a pair this wave's keys see:
+  // in a masked tile, blocks entirely before the wave's keys are skipped by
+  // the score products (their probabilities are zero).
+  auto runs = [&](bool masked, int it, int qs) TAM_INLINE {
+    return !(masked && CAUSAL && it * kKBR + qs * 32 + 31 + dlt < kvb0);
+  };
+
+  // x = A B^T over the head dim for the rows of the tile at rr and this
+  // wave's keys: S = Q K^T (P role) or dP = dO V^T (dS role); lane holds key
+  // kvrow, rows it*64 + 32qs + 8(v/4) + 4half + v%4.
+  auto rows_by_keys = [&](bool masked, int it, f32x16 (&x)[2]) TAM_INLINE {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       x[qs] = f32x16{};
-      if (!run[qs]) continue;
+      if (!runs(masked, it, qs)) continue;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        x[qs] = mfma32(*reinterpret_cast<const bf16x8*>(smem + AB + qs * 32 * T::ROW_BYTES + rr[ks]), kvf[ks],
-                       x[qs]);
+        x[qs] = mfma32(*reinterpret_cast<const bf16x8*>(smem + rr[ks] + qs * 32 * T::ROW_BYTES), kvf[ks], x[qs]);
     }
-    bf16x8 hi[2][2], lo[2][2];
-    if (vrole) {
+  };
+
+  // acc^T += A^T G for the rows of the tile at tt (read transposed) and the
+  // gradient-side operand G given as hi + lo bf16 pairs: dV^T += dO^T P (P
+  // role) or dK^T += Q^T dS (dS role). It runs for both row blocks of every
+  // tile (a skipped block contributes exact zeros), and each role has one
+  // copy of it per loop body: every accumulator value then feeds exactly one
+  // matrix instruction, so the compiler accumulates in place instead of
+  // keeping a second copy of dV^T/dK^T.
+  auto accumulate = [&](const bf16x8 (&hi)[2][2], const bf16x8 (&lo)[2][2]) TAM_INLINE {
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 l2 = *reinterpret_cast<const f32x4*>(Fs + qs * 32 + 8 * i + 4 * half);
-          // dropout bytes of rows R .. R + 3 (word r) for this lane's key (byte kvrow % 4)
-          u32x4 dw = {0u, 0u, 0u, 0u};
-          if (DROP)
-            dw = philox4x32_10((uint32_t)kvrow >> 2, (uint32_t)(it * kKBR + qs * 32 + 8 * i + 4 * half) >> 2, bhq,
-                               0u, a.drop.seed_lo, a.drop.seed_hi);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = 4 * i + r;
-            float e = fast_exp2(fmaf(x[qs][v], c, -l2[r]));
-            if (MASKED) {
-              const int qrow = it * kKBR + qs * 32 + 8 * i + 4 * half + r;
-              const bool ok = run[qs] && qrow < Sq && kvrow < Sk && (!CAUSAL || kvrow <= qrow + dlt);
-              e = ok ? e : 0.f;
-            }
-            if (DROP) {
-              // P goes to the partner with the sign carrying the mask; dV uses
-              // the kept probabilities scaled by r
-              const bool keep = drop_keep(dw[r], kvrow & 3, a.drop.t);
-              pbuf[(16 * qs + v) * 64] = keep ? e : -e;
-              p[v] = keep ? e * a.drop.r : 0.f;
-            } else {
-              p[v] = e;
-              pbuf[(16 * qs + v) * 64] = e;
-            }
-          }
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) split_bf16x8(p + 8 * k2, &hi[qs][k2], &lo[qs][k2]);
-      }
-    }
-    __syncthreads();  // P handed over
-    if (!vrole) {
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        float ds[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 dl4 = *reinterpret_cast<const f32x4*>(Fs + kKBR + qs * 32 + 8 * i + 4 * half);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = 4 * i + r;
-            const float pv = pbuf[(16 * qs + v) * 64];
-            ds[v] = DROP ? fabsf(pv) * ((__builtin_signbit(pv) ? 0.f : a.drop.r) * x[qs][v] - dl4[r])
-                         : pv * (x[qs][v] - dl4[r]);
-          }
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) split_bf16x8(ds + 8 * k2, &hi[qs][k2], &lo[qs][k2]);
-      }
-    }
-    // dV^T += dO^T P (P role) or dK^T += Q^T dS (dS role); the A operand is read
-    // transposed from the other streamed tile.
-    const int TB = vrole ? DOB : QB;
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      if (!run[qs]) continue;
+    for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int ro = TB + (qs * 32 + k2 * 16) * T::ROW_BYTES;
+          const int ro = (qs * 32 + k2 * 16) * T::ROW_BYTES;
           const bf16x8 at = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(smem + ro + tt[db][0]),
                                              reinterpret_cast<const uint16_t*>(smem + ro + tt[db][1]));
           acc[db] = mfma32(at, hi[qs][k2], acc[db]);
           acc[db] = mfma32(at, lo[qs][k2], acc[db]);
         }
+  };
+
+  // P role, one step: P = exp2(S c - lse2) with the tile's mask, to the
+  // partner (with dropout: the sign carries the keep bit) and as hi + lo
+  // pairs for dV (with dropout: the kept probabilities scaled by r).
+  auto probabilities = [&](auto masked_tag, int st, int it, uint32_t bhq, bool masked, const f32x16 (&x)[2],
+                           bf16x8 (&hi)[2][2], bf16x8 (&lo)[2][2]) TAM_INLINE {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const float* Fs = reinterpret_cast<const float*>(smem + f_at(st));
+    float* pb = pb_at(st);
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const bool run = runs(masked, it, qs);
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(Fs + qs * 32 + 8 * i + 4 * half);
+        // dropout bytes of rows R .. R + 3 (word r) for this lane's key (byte kvrow % 4)
+        u32x4 dw = {0u, 0u, 0u, 0u};
+        if (DROP)
+          dw = philox4x32_10((uint32_t)kvrow >> 2, (uint32_t)(it * kKBR + qs * 32 + 8 * i + 4 * half) >> 2, bhq, 0u,
+                             a.drop.seed_lo, a.drop.seed_hi);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = 4 * i + r;
+          float e = fast_exp2(fmaf(x[qs][v], c, -l2[r]));
+          if (MASKED) {
+            const int qrow = it * kKBR + qs * 32 + 8 * i + 4 * half + r;
+            const bool ok = run && qrow < Sq && kvrow < Sk && (!CAUSAL || kvrow <= qrow + dlt);
+            e = ok ? e : 0.f;
+          }
+          if (DROP) {
+            const bool keep = drop_keep(dw[r], kvrow & 3, a.drop.t);
+            pb[(16 * qs + v) * 64] = keep ? e : -e;
+            p[v] = keep ? e * a.drop.r : 0.f;
+          } else {
+            p[v] = e;
+            pb[(16 * qs + v) * 64] = e;
+          }
+        }
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) split_bf16x8(p + 8 * k2, &hi[qs][k2], &lo[qs][k2]);
     }
   };
 
-  auto step = [&](auto stage_tag, int st) TAM_INLINE {
-    constexpr int STG = decltype(stage_tag)::value;
-    if (st + 1 < nsteps) issue(st + 1, STG ^ 1);
-    const int it = step_tile(st);
-    // the whole workgroup takes the same branch: the tile meets the diagonal of
-    // the unit's 128 keys, or the end of the sequence
-    const bool masked = (CAUSAL && it * kKBR + dlt < kvt0 + kKBC) || it * kKBR + kKBR > Sq || kvt0 + kKBC > Sk;
-    const uint32_t bhq = (uint32_t)(b * a.Hq + step_head(st));
-    if (masked)
-      tile(std::true_type{}, stage_tag, it, bhq);
-    else
-      tile(std::false_type{}, stage_tag, it, bhq);
-    wait_loads();
-    __syncthreads();
+  // dS role, second half of step st: dS = P (dP - Delta) from the partner's P
+  // and the dP held in x since the step before, as hi + lo pairs.
+  auto grad_scores = [&](int st, const f32x16 (&x)[2], bf16x8 (&hi)[2][2], bf16x8 (&lo)[2][2]) TAM_INLINE {
+    const float* Fs = reinterpret_cast<const float*>(smem + f_at(st));
+    const float* pb = pb_at(st);
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 dl4 = *reinterpret_cast<const f32x4*>(Fs + kKBR + qs * 32 + 8 * i + 4 * half);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = 4 * i + r;
+          const float pv = pb[(16 * qs + v) * 64];
+          ds[v] = DROP ? fabsf(pv) * ((__builtin_signbit(pv) ? 0.f : a.drop.r) * x[qs][v] - dl4[r])
+                       : pv * (x[qs][v] - dl4[r]);
+        }
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) split_bf16x8(ds + 8 * k2, &hi[qs][k2], &lo[qs][k2]);
+    }
   };
 
-  if (nsteps > 0) issue(0, 0);
-  wait_loads();
-  __syncthreads();
-  for (int st = 0; st < nsteps; st += 2) {
-    step(std::integral_constant<int, 0>{}, st);
-    if (st + 1 < nsteps) step(std::integral_constant<int, 1>{}, st + 1);
+  // Software pipeline with one barrier per phase. In phase t the P wave of
+  // each pair runs step t whole (S, P, dV) while its dS partner finishes step
+  // t - 1 (whose P was handed over in phase t - 1: dS, dK) and then computes
+  // dP of step t. The two waves of a pair share a SIMD, so the exponentials of
+  // one overlap the matrix products of the other. Step t + 1's tiles load
+  // meanwhile: its Q stage last served step t - 2, its dO stage step t - 1.
+  // Both roles pass nsteps + 1 barriers after the first load.
+  if (nsteps > 0) {
+    Cursor cur = {h_first, NQ - 1};   // step t
+    issue(0, cur);
+    wait_loads();
+    __syncthreads();
+    Cursor nxt = cur;                 // step t + 1
+    advance(nxt);
+    if (vrole) {
+      for (int st = 0; st < nsteps; ++st) {
+        if (st + 1 < nsteps) issue(st + 1, nxt);
+        const int it = cur.it;
+        const bool masked = masked_at(it);
+        const uint32_t bhq = (uint32_t)(b * a.Hq + cur.h);
+        f32x16 x[2];
+        rows_by_keys(masked, it, x);
+        bf16x8 hi[2][2], lo[2][2];
+        if (masked)
+          probabilities(std::true_type{}, st, it, bhq, masked, x, hi, lo);
+        else
+          probabilities(std::false_type{}, st, it, bhq, masked, x, hi, lo);
+        accumulate(hi, lo);
+        move_rr(q_next(st));
+        move_tt(do_next(st));
+        advance(cur);
+        advance(nxt);
+        wait_loads();
+        __syncthreads();
+      }
+      __syncthreads();  // the partner's last phase
+    } else {
+      f32x16 x[2];  // dP of the step before, carried over the barrier
+      if (nsteps > 1) issue(1, nxt);
+      rows_by_keys(masked_at(cur.it), cur.it, x);
+      move_rr(do_next(0));
+      advance(cur);
+      advance(nxt);
+      wait_loads();
+      __syncthreads();
+      for (int st = 1; st < nsteps; ++st) {
+        if (st + 1 < nsteps) issue(st + 1, nxt);
+        bf16x8 hi[2][2], lo[2][2];
+        grad_scores(st - 1, x, hi, lo);
+        accumulate(hi, lo);
+        move_tt(q_next(st - 1));
+        rows_by_keys(masked_at(cur.it), cur.it, x);
+        move_rr(do_next(st));
+        advance(cur);
+        advance(nxt);
+        wait_loads();
+        __syncthreads();
+      }
+      bf16x8 hi[2][2], lo[2][2];
+      grad_scores(nsteps - 1, x, hi, lo);
+      accumulate(hi, lo);
+      __syncthreads();
+    }
   }
 
   // lane holds key kvrow, head-dim entries 32db + 8i + 4half + (0..3)
