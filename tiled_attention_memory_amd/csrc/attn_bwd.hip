@@ -12,7 +12,9 @@
 // Kernels, all on the caller's stream:
 //   1. prep:  Delta~ = sum_d dO_id O_id from the stored bf16 O, and
 //             LSE * log2(e), per query row (workspace).
-//   2. dq:    query-stationary, like the forward pass: dQ^T += K^T dS^T. It also
+//   2. dq:    query-stationary, like the forward pass: dQ^T += K^T dS^T, with
+//             the same wave-pair split as kernel 3 (one wave computes S, P and
+//             P K, its partner dP, dS and dQ one key tile behind). It also
 //             makes Delta exact: with dS~ = P (dP - Delta~) and sum_j P_ij = 1,
 //             Delta_i - Delta~_i = sum_j dS~_ij =: c_i, so
 //             dQ_i = scale (sum_j dS~_ij K_j - c_i sum_j P_ij K_j), and the exact
@@ -565,15 +567,18 @@ struct DqArgs {
   TileSched sched;
 };
 
-// LDS layout of the dQ kernel: two stages of K and V tiles, then the
-// probabilities one wave of each pair hands to the other.
+// LDS layout of the dQ kernel. The two waves of a pair work one key tile
+// apart (see the kernel), so K is kept in three stages (tile t in stage t % 3),
+// V in two (t % 2), and the probabilities one wave of each pair hands to the
+// other in two.
 template <int D>
 struct DqLayout {
   using T = SwzTile<D>;
-  static constexpr int K0 = 0, V0 = T::BYTES, K1 = 2 * T::BYTES, V1 = 3 * T::BYTES;
-  static constexpr int PB = 4 * T::BYTES;
+  static constexpr int K0 = 0, V0 = 3 * T::BYTES;
+  static constexpr int PB = 5 * T::BYTES;
   static constexpr int PB_BLOCK = 32 * kQBC * 4;  // 32 rows x 64 keys fp32
-  static constexpr int BYTES = PB + 4 * PB_BLOCK;
+  static constexpr int PB_STAGE = 4 * PB_BLOCK;
+  static constexpr int BYTES = PB + 2 * PB_STAGE;
   static_assert(4 * (D / 32) * 16 * 64 * 4 <= PB, "final hand-off fits in the stages");
 };
 
@@ -586,6 +591,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
   constexpr int DB = D / 32;
   constexpr int NLD = T::LOADS / 4;   // K and V loads per wave per tile
   static_assert(kQBC == T::ROWS && kQBR == 128, "tile sizes");
+  static_assert(L::BYTES <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
 
   int bh, qt;
@@ -618,38 +624,56 @@ void attn_bwd_dq_kernel(DqArgs a) {
   }
   const float rowval = qrow < Sq ? (prole ? a.lse2 : a.delta)[(size_t)bh * Sq + qrow] : 0.f;  // lse2 or Delta~
 
-  // per-lane LDS offsets, fixed for every tile (see SwzTile)
+  // Per-lane LDS offsets (see SwzTile) into the stage this wave reads next:
+  // roff for the key-by-row products (K for the P role, V for the dS role),
+  // toff for the transposed K reads. They move to the next stage in place, by
+  // a uniform step, so that a runtime stage costs no registers.
   const int i16 = lane & 15;
   const int dsub = 16 * ((lane >> 4) & 1);
   int roff[KS], toff[DB][2], loff[NLD];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) roff[ks] = T::chunk_off(col, 2 * ks + half);
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = (prole ? L::K0 : L::V0) + T::chunk_off(col, 2 * ks + half);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi)
-      toff[db][hi] = T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
+      toff[db][hi] = L::K0 + T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
 #pragma unroll
   for (int i = 0; i < NLD; ++i) loff[i] = T::load_src((wave * NLD + i) % T::LOADS, lane);
-  // this lane's slots of the P hand-off block: key v of 32-key block kb at (16 kb + v) * 64 + lane
-  float* pbuf = reinterpret_cast<float*>(smem + L::PB + rblk * L::PB_BLOCK) + lane;
+  // stage step after tile j: K stages cycle through three, V stages through two
+  auto k_next = [&](int j) TAM_INLINE { return j % 3 == 2 ? -2 * T::BYTES : T::BYTES; };
+  auto v_next = [&](int j) TAM_INLINE { return (j & 1) ? -T::BYTES : T::BYTES; };
+  auto move_roff = [&](int by) TAM_INLINE {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) roff[ks] += by;
+  };
+  auto move_toff = [&](int by) TAM_INLINE {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) toff[db][hi] += by;
+  };
+  // this lane's slots of the P hand-off block of stage 0: key v of 32-key
+  // block kb at (16 kb + v) * 64 + lane
+  float* const pbuf = reinterpret_cast<float*>(smem + L::PB + rblk * L::PB_BLOCK) + lane;
+  auto pb_at = [&](int j) TAM_INLINE { return pbuf + (j & 1) * (L::PB_STAGE / 4); };
 
   const int last_row = min(q0 + kQBR, Sq) - 1;
   const int n_kv = (Sk + kQBC - 1) / kQBC;
   // the last key any row of the unit may see is last_row + dlt
   const int ntiles = CAUSAL ? (last_row + dlt < 0 ? 0 : min(n_kv, (last_row + dlt) / kQBC + 1)) : n_kv;
 
-  // K and V tiles straight into stage `stg`; rows past Sk read as zeros.
-  auto issue = [&](int j, int stg) TAM_INLINE {
+  // K and V tiles of key tile j straight into their stages; rows past Sk read as zeros.
+  auto issue = [&](int j) TAM_INLINE {
     const int row0 = j * kQBC;
     const int bytes = (Sk - row0) * D * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)row0 * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)row0 * D, bytes);
-    const uint32_t base = lds0 + (stg ? L::K1 : L::K0);
+    const uint32_t kb = lds0 + L::K0 + (j % 3) * T::BYTES, vb = lds0 + L::V0 + (j & 1) * T::BYTES;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int gi = wave * NLD + i, which = gi / T::LOADS, li = gi % T::LOADS;
-      dma16(which == 0 ? rk : rv, base + which * T::BYTES + li * 1024, loff[i]);
+      dma16(which == 0 ? rk : rv, (which == 0 ? kb : vb) + li * 1024, loff[i]);
     }
   };
 
@@ -659,93 +683,97 @@ void attn_bwd_dq_kernel(DqArgs a) {
   float csum = 0.f;  // dS role: this lane's half of c = sum_j dS~_j for its row
   const float c = a.c;
 
-  // One 64-key tile as two 32-key blocks against this pair's 32 rows. MASKED:
-  // the tile meets the pair's diagonal or the end of the sequence; hidden
-  // pairs get P = 0. The P role computes S and P, hands P over and accumulates
-  // P K; the dS role computes dP, takes P, forms dS~ and accumulates dS~ K. The
-  // barrier in the middle orders the hand-off; every wave reaches it.
-  //
-  // S^T = K Q^T or dP^T = V dO^T: lane holds keys kv0 + 32kb + 8(v/4) + 4half + v%4 of row qrow.
-  auto scores = [&](int AB, f32x16 (&x)[2]) TAM_INLINE {
+  // Key tiles of 64 keys, as two 32-key blocks, against this pair's 32 rows.
+  // A tile is active for the pair when some key of it is visible to one of
+  // its rows; it is masked when it meets the pair's diagonal or the end of
+  // the sequence, and then hidden pairs get P = 0.
+  auto active_at = [&](int j) TAM_INLINE { return !CAUSAL || j * kQBC <= wrow0 + 31 + dlt; };
+  auto masked_at = [&](int j) TAM_INLINE {
+    return (j * kQBC + kQBC > Sk) || (CAUSAL && j * kQBC + kQBC - 1 > wrow0 + dlt);
+  };
+
+  // S^T = K Q^T (P role) or dP^T = V dO^T (dS role) from the tile at roff:
+  // lane holds keys 32kb + 8(v/4) + 4half + v%4 of row qrow. Skipped (zero)
+  // for a tile no row of the pair sees.
+  auto scores = [&](bool active, f32x16 (&x)[2]) TAM_INLINE {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) x[kb] = f32x16{};
+    if (!active) return;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        x[kb] = mfma32(*reinterpret_cast<const bf16x8*>(smem + AB + kb * 32 * T::ROW_BYTES + roff[ks]), xf[ks], x[kb]);
+        x[kb] = mfma32(*reinterpret_cast<const bf16x8*>(smem + roff[ks] + kb * 32 * T::ROW_BYTES), xf[ks], x[kb]);
   };
-  // K^T rows kb*32 + k2*16 .. +15 of the tile as A operands, read transposed
-  auto kt_operands = [&](int KB, int kb, int k2, bf16x8 (&a_k)[DB]) TAM_INLINE {
-    const int ro = KB + (kb * 32 + k2 * 16) * T::ROW_BYTES;
+  // K^T rows kb*32 + k2*16 .. +15 of the tile at toff as A operands, read transposed
+  auto kt_operands = [&](int kb, int k2, bf16x8 (&a_k)[DB]) TAM_INLINE {
+    const int ro = (kb * 32 + k2 * 16) * T::ROW_BYTES;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
       a_k[db] = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(smem + ro + toff[db][0]),
                                  reinterpret_cast<const uint16_t*>(smem + ro + toff[db][1]));
   };
 
-  auto tile_p = [&](auto masked_tag, auto stage_tag, int kv0, bool active) TAM_INLINE {
+  // P role, one tile: P = exp2(S c - lse2) with the tile's mask, handed to the
+  // partner (with dropout: the sign carries the keep bit), and as bf16 B
+  // operands (before dropout) for P K.
+  auto probabilities = [&](auto masked_tag, int j, bool active, const f32x16 (&x)[2],
+                           bf16x8 (&ph)[2][2]) TAM_INLINE {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    constexpr int KB = decltype(stage_tag)::value ? L::K1 : L::K0;
-    bf16x8 ph[2][2];
-    if (active) {
-      f32x16 x[2];
-      scores(KB, x);
+    const int kv0 = j * kQBC;
+    float* pb = pb_at(j);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float pf[16];
-        uint32_t dbytes = 0u;
+    for (int kb = 0; kb < 2; ++kb) {
+      float pf[16];
+      uint32_t dbytes = 0u;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float e = fast_exp2(fmaf(x[kb][v], c, -rowval));
-          if (MASKED) {
-            const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-            const bool ok = kv < Sk && (!CAUSAL || kv <= qrow + dlt);
-            e = ok ? e : 0.f;
-          }
-          pf[v] = e;
-          if (DROP) {
-            // P K uses P before dropout; the partner gets P with the sign carrying the mask
-            if ((v & 3) == 0)
-              dbytes = drop_row_bytes(a.drop, (uint32_t)bh, (uint32_t)qrow,
-                                      (uint32_t)(kv0 + kb * 32 + 8 * (v >> 2) + 4 * half) >> 2);
-            pbuf[(16 * kb + v) * 64] = drop_keep(dbytes, v & 3, a.drop.t) ? e : -e;
-          } else {
-            pbuf[(16 * kb + v) * 64] = e;
-          }
+      for (int v = 0; v < 16; ++v) {
+        float e = fast_exp2(fmaf(x[kb][v], c, -rowval));
+        if (MASKED) {
+          const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          const bool ok = active && kv < Sk && (!CAUSAL || kv <= qrow + dlt);
+          e = ok ? e : 0.f;
         }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) ph[kb][k2] = pack_bf16x8(pf + 8 * k2);
+        pf[v] = e;
+        if (DROP) {
+          if ((v & 3) == 0)
+            dbytes = drop_row_bytes(a.drop, (uint32_t)bh, (uint32_t)qrow,
+                                    (uint32_t)(kv0 + kb * 32 + 8 * (v >> 2) + 4 * half) >> 2);
+          pb[(16 * kb + v) * 64] = drop_keep(dbytes, v & 3, a.drop.t) ? e : -e;
+        } else {
+          pb[(16 * kb + v) * 64] = e;
+        }
       }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) ph[kb][k2] = pack_bf16x8(pf + 8 * k2);
     }
-    __syncthreads();  // P handed over
-    if (!active) return;
-    // (P K)^T += K^T P^T
+  };
+  // (P K)^T += K^T P^T. It runs for every tile (an inactive one adds exact
+  // zeros) and appears once in the loop, so that each accumulator value feeds
+  // one matrix instruction and is updated in place.
+  auto pk_product = [&](const bf16x8 (&ph)[2][2]) TAM_INLINE {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         bf16x8 a_k[DB];
-        kt_operands(KB, kb, k2, a_k);
+        kt_operands(kb, k2, a_k);
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], ph[kb][k2], acc[db]);
       }
   };
 
-  auto tile_ds = [&](auto stage_tag, bool active) TAM_INLINE {
-    constexpr int STG = decltype(stage_tag)::value;
-    constexpr int KB = STG ? L::K1 : L::K0, VB = STG ? L::V1 : L::V0;
-    f32x16 x[2];
-    if (active) scores(VB, x);
-    __syncthreads();  // P handed over
-    if (!active) return;
-    // dQ^T += K^T dS~^T, hi and lo parts
+  // dS role, second half of tile j: dS~ = P (dP - Delta~) from the partner's
+  // P and the dP held since the step before, c += sum dS~, and dQ^T +=
+  // K^T dS~^T with hi and lo parts (once per loop body, for every tile).
+  auto ds_tile = [&](int j, const f32x16 (&x)[2]) TAM_INLINE {
+    const float* pb = pb_at(j);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float ds[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float pv = pbuf[(16 * kb + v) * 64];
+        const float pv = pb[(16 * kb + v) * 64];
         ds[v] = DROP ? fabsf(pv) * ((__builtin_signbit(pv) ? 0.f : a.drop.r) * x[kb][v] - rowval)
                      : pv * (x[kb][v] - rowval);
         csum += ds[v];
@@ -756,7 +784,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         bf16x8 a_k[DB];
-        kt_operands(KB, kb, k2, a_k);
+        kt_operands(kb, k2, a_k);
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], dh[k2], acc[db]);
 #pragma unroll
@@ -765,31 +793,54 @@ void attn_bwd_dq_kernel(DqArgs a) {
     }
   };
 
-  auto step = [&](auto stage_tag, int j) TAM_INLINE {
-    constexpr int STG = decltype(stage_tag)::value;
-    if (j + 1 < ntiles) issue(j + 1, STG ^ 1);
-    const int kv0 = j * kQBC;
-    const bool active = !CAUSAL || kv0 <= wrow0 + 31 + dlt;
-    if (prole) {
-      // uniform per wave: the tile meets the pair's diagonal or the end of the sequence
-      const bool masked = (kv0 + kQBC > Sk) || (CAUSAL && kv0 + kQBC - 1 > wrow0 + dlt);
-      if (masked)
-        tile_p(std::true_type{}, stage_tag, kv0, active);
-      else
-        tile_p(std::false_type{}, stage_tag, kv0, active);
-    } else {
-      tile_ds(stage_tag, active);
-    }
+  // Software pipeline with one barrier per phase. In phase t the P wave of
+  // each pair runs tile t whole (S, P, P K) while its dS partner finishes tile
+  // t - 1 (whose P was handed over in phase t - 1: dS, dQ) and then computes
+  // dP of tile t. The two waves of a pair share a SIMD, so the exponentials of
+  // one overlap the matrix products of the other. Tile t + 1 loads meanwhile:
+  // its K stage last served tile t - 2, its V stage tile t - 1. Both roles
+  // pass ntiles + 2 barriers.
+  if (ntiles > 0) {
+    issue(0);
     wait_loads();
     __syncthreads();
-  };
-
-  if (ntiles > 0) issue(0, 0);
-  wait_loads();
-  __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
-    step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1);
+    if (prole) {
+      for (int j = 0; j < ntiles; ++j) {
+        if (j + 1 < ntiles) issue(j + 1);
+        const bool active = active_at(j);
+        f32x16 x[2];
+        scores(active, x);
+        bf16x8 ph[2][2];
+        if (masked_at(j))
+          probabilities(std::true_type{}, j, active, x, ph);
+        else
+          probabilities(std::false_type{}, j, active, x, ph);
+        pk_product(ph);
+        move_roff(k_next(j));
+        move_toff(k_next(j));
+        wait_loads();
+        __syncthreads();
+      }
+      __syncthreads();  // the partner's last phase
+    } else {
+      f32x16 x[2];  // dP of the tile before, carried over the barrier
+      if (ntiles > 1) issue(1);
+      scores(active_at(0), x);
+      move_roff(v_next(0));
+      wait_loads();
+      __syncthreads();
+      for (int j = 1; j < ntiles; ++j) {
+        if (j + 1 < ntiles) issue(j + 1);
+        ds_tile(j - 1, x);
+        move_toff(k_next(j - 1));
+        scores(active_at(j), x);
+        move_roff(v_next(j));
+        wait_loads();
+        __syncthreads();
+      }
+      ds_tile(ntiles - 1, x);
+      __syncthreads();
+    }
   }
 
   if (a.acc_dq) {
