@@ -368,7 +368,8 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
           float e = fast_exp2(fmaf(x[qs][v], c, -l2[r]));
           if (MASKED) {
             const int qrow = it * kKBR + qs * 32 + 8 * i + 4 * half + r;
-            const bool ok = run && qrow < Sq && kvrow < Sk && (!CAUSAL || kvrow <= qrow + dlt);
+            // bitwise &: every term is evaluated, so the select stays branch-free
+            const bool ok = run & (qrow < Sq) & (kvrow < Sk) & (!CAUSAL | (kvrow <= qrow + dlt));
             e = ok ? e : 0.f;
           }
           if (DROP) {
@@ -731,7 +732,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
         float e = fast_exp2(fmaf(x[kb][v], c, -rowval));
         if (MASKED) {
           const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          const bool ok = active && kv < Sk && (!CAUSAL || kv <= qrow + dlt);
+          const bool ok = active & (kv < Sk) & (!CAUSAL | (kv <= qrow + dlt));  // branch-free
           e = ok ? e : 0.f;
         }
         pf[v] = e;
@@ -830,8 +831,8 @@ void attn_bwd_dq_kernel(DqArgs a) {
       wait_loads();
       __syncthreads();
       for (int j = 1; j < ntiles; ++j) {
-        if (j + 1 < ntiles) issue(j + 1);
         ds_tile(j - 1, x);
+        if (j + 1 < ntiles) issue(j + 1);  // after the products: its issue stalls overlap them
         move_toff(k_next(j - 1));
         scores(active_at(j), x);
         move_roff(v_next(j));
