@@ -68,6 +68,69 @@ class Hip:
     def destroy(self, ev):
         self.lib.hipEventDestroy(ev)
 
+    def attribute(self, attr, device=0):
+        out = ctypes.c_int()
+        self.check(self.lib.hipDeviceGetAttribute(ctypes.byref(out), attr, device), "hipDeviceGetAttribute")
+        return out.value
+
+
+# hipDeviceAttribute_t values (hip_runtime_api.h)
+HIP_ATTR_CLOCK_RATE_KHZ = 5
+HIP_ATTR_MEMORY_CLOCK_RATE_KHZ = 60
+HIP_ATTR_MULTIPROCESSOR_COUNT = 63
+
+
+def device_facts(hip):
+    """CU count and peak engine clock as the runtime reports them, and the bf16 dense peak they imply
+    (4096 flop per clock per CU on gfx950)."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    cus = hip.attribute(HIP_ATTR_MULTIPROCESSOR_COUNT)
+    sclk_mhz = hip.attribute(HIP_ATTR_CLOCK_RATE_KHZ) / 1e3
+    return {"name": props.name, "arch": props.gcnArchName, "cus": cus, "max_sclk_mhz": sclk_mhz,
+            "max_mclk_mhz": hip.attribute(HIP_ATTR_MEMORY_CLOCK_RATE_KHZ) / 1e3,
+            "bf16_peak_at_max_sclk_tflops": round(cus * 4096 * sclk_mhz * 1e6 / 1e12, 1)}
+
+
+def hbm_probe(hip, mib, reps=20):
+    """Achievable HBM bandwidth with plain library kernels on buffers of `mib` MiB: sequential
+    write (fill), read (sum), copy, and a gather of random 4 KiB blocks. GB/s = bytes moved over
+    the median event time of `reps` runs after two warm-up runs."""
+    import torch
+    n = (mib << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    rows = a.view(-1, 1024)                     # 4 KiB rows
+    g = torch.Generator(device="cuda").manual_seed(1)
+    idx = torch.randperm(rows.shape[0], device="cuda", generator=g)[: rows.shape[0] // 2]
+    out_rows = torch.empty((idx.numel(), 1024), dtype=torch.float32, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+    size = a.numel() * 4
+    cases = {
+        "write": (lambda: a.fill_(2.0), size),
+        "read": (lambda: a.sum(), size),
+        "copy": (lambda: b.copy_(a), 2 * size),
+        "gather_4k_random": (lambda: torch.index_select(rows, 0, idx, out=out_rows), 2 * idx.numel() * 4096),
+    }
+    res = {}
+    for name, (fn, nbytes) in cases.items():
+        for _ in range(2):
+            fn()
+        times = []
+        for _ in range(reps):
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, sh)
+            fn()
+            hip.record(e1, sh)
+            torch.cuda.synchronize()
+            times.append(hip.ms(e0, e1))
+            hip.destroy(e0)
+            hip.destroy(e1)
+        times.sort()
+        med = times[len(times) // 2]
+        res[name] = {"bytes": nbytes, "ms_median": round(med, 4), "gbps": round(nbytes / (med * 1e-3) / 1e9, 1)}
+    return res
+
 
 def kernel_source_sha():
     h = hashlib.sha256()
@@ -292,6 +355,9 @@ def main():
                          "memory-side cache start cold (for the short, bandwidth-bound shapes); "
                          "the step time is then the sum of the per-kernel event times")
     ap.add_argument("--cpu-groups", type=int, default=8)
+    ap.add_argument("--hbm-probe", type=int, default=0, metavar="MIB",
+                    help="instead of attention: achievable HBM bandwidth of plain library kernels "
+                         "(fill, sum, copy, random 4 KiB gather) on MIB-sized buffers")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy a MIB-mebibyte device buffer 3 times (a plain copy "
                          "kernel of known size, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -311,6 +377,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     tam.load()  # fail loudly if the HIP library is missing
+    if args.hbm_probe:
+        hip = Hip()
+        res = hbm_probe(hip, args.hbm_probe)
+        print(json.dumps({"metric": "achievable HBM bandwidth of library kernels", "value": res["copy"]["gbps"],
+                          "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "peak_gbps": 8000.0,
+                          "buffer_mib": args.hbm_probe, "probes": res, "device": device_facts(hip)}))
+        return
     w = wl.BY_NAME[args.workload]
     log(f"[bench] workload {w.name}: {w.describe()}")
     if args.cp:
@@ -382,6 +455,9 @@ def main():
 
     def avg(pairs):
         return sum(hip.ms(a, b) for a, b in pairs) / len(pairs)
+
+    # per-step times, forward start to backward end (the kernels' own events)
+    steps_ms = sorted(hip.ms(ev_f[i][0], ev_b[i][tam.BWD_EVENTS - 1]) for i in range(K))
 
     per = {
         "attn_fwd_kernel": avg(ev_f),
@@ -455,6 +531,8 @@ def main():
                    "seq_len": w.S, "parallelism": "none", **({"dropout": args.dropout} if args.dropout else {}),
                    **({"rope_base": args.rope} if args.rope else {})},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "ms_step_median": round(steps_ms[K // 2], 4),
+        "ms_step_min": round(steps_ms[0], 4),
         "fwd_tflops": round(w.fwd_flops() / (per["attn_fwd_kernel"] * 1e-3) / 1e12, 1),
         "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),
         # algorithmic bytes (each tensor once) over the pass time, for the short shapes
@@ -462,6 +540,7 @@ def main():
         "bwd_alg_gbps": round(alg_bytes(w)[1] / (bwd_ms * 1e-3) / 1e9, 1),
         "kernels": kernels,
         "roofline": roofline,
+        "device": device_facts(hip),
     }
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
