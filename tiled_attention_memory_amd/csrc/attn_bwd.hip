@@ -308,16 +308,31 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 
   // x = A B^T over the head dim for the rows of the tile at rr and this
   // wave's keys: S = Q K^T (P role) or dP = dO V^T (dS role); lane holds key
-  // kvrow, rows it*64 + 32qs + 8(v/4) + 4half + v%4.
-  auto rows_by_keys = [&](bool masked, int it, f32x16 (&x)[2]) TAM_INLINE {
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      x[qs] = f32x16{};
-      if (!runs(masked, it, qs)) continue;
+  // kvrow, rows it*64 + 32qs + 8(v/4) + 4half + v%4. The two row blocks'
+  // chains are interleaved (each operand read then has a product of the other
+  // chain to hide behind). In a masked tile a block entirely before the
+  // wave's keys is skipped; block 1 sees a key whenever block 0 does.
+  auto rows_by_keys = [&](auto masked_tag, int it, f32x16 (&x)[2]) TAM_INLINE {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    x[0] = f32x16{};
+    x[1] = f32x16{};
+    if (runs(MASKED, it, 0)) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        x[qs] = mfma32(*reinterpret_cast<const bf16x8*>(smem + rr[ks] + qs * 32 * T::ROW_BYTES), kvf[ks], x[qs]);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+          x[qs] = mfma32(*reinterpret_cast<const bf16x8*>(smem + rr[ks] + qs * 32 * T::ROW_BYTES), kvf[ks], x[qs]);
+    } else if (runs(MASKED, it, 1)) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        x[1] = mfma32(*reinterpret_cast<const bf16x8*>(smem + rr[ks] + 32 * T::ROW_BYTES), kvf[ks], x[1]);
     }
+  };
+  auto rows_by_keys_at = [&](bool masked, int it, f32x16 (&x)[2]) TAM_INLINE {
+    if (masked)
+      rows_by_keys(std::true_type{}, it, x);
+    else
+      rows_by_keys(std::false_type{}, it, x);
   };
 
   // acc^T += A^T G for the rows of the tile at tt (read transposed) and the
@@ -432,7 +447,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
         const bool masked = masked_at(it);
         const uint32_t bhq = (uint32_t)(b * a.Hq + cur.h);
         f32x16 x[2];
-        rows_by_keys(masked, it, x);
+        rows_by_keys_at(masked, it, x);
         bf16x8 hi[2][2], lo[2][2];
         if (masked)
           probabilities(std::true_type{}, st, it, bhq, masked, x, hi, lo);
@@ -450,7 +465,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
     } else {
       f32x16 x[2];  // dP of the step before, carried over the barrier
       if (nsteps > 1) issue(1, nxt);
-      rows_by_keys(masked_at(cur.it), cur.it, x);
+      rows_by_keys_at(masked_at(cur.it), cur.it, x);
       move_rr(do_next(0));
       advance(cur);
       advance(nxt);
@@ -462,7 +477,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
         grad_scores(st - 1, x, hi, lo);
         accumulate(hi, lo);
         move_tt(q_next(st - 1));
-        rows_by_keys(masked_at(cur.it), cur.it, x);
+        rows_by_keys_at(masked_at(cur.it), cur.it, x);
         move_rr(do_next(st));
         advance(cur);
         advance(nxt);
