@@ -37,7 +37,11 @@
 // results are bitwise reproducible.
 #include <math.h>
 
+#include <algorithm>
+#include <functional>
+#include <queue>
 #include <type_traits>
+#include <vector>
 
 #include "attn_device.h"
 #include "attn_launch.h"
@@ -58,16 +62,71 @@ constexpr int kTargetUnits = 1024;
 // ---------------------------------------------------------------------------
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int choose_head_split(const AttnShape& sh) {
-  const int g = sh.Hq / sh.Hkv;
-  const long long units = (long long)sh.B * sh.Hkv * ((sh.Sk + kKBC - 1) / kKBC);
-  int ns = 1;
-  while (units * ns < kTargetUnits && ns < g) {
-    int next = ns + 1;
-    while (g % next) ++next;
-    ns = next;
+// Head subsets per (batch, kv head, key tile) unit of the dK/dV kernel. More
+// subsets give more, shorter units, which balance better over the CUs, at the
+// cost of fp32 partials and the reduce pass.
+//
+// Whole-sequence calls: the smallest divisor of g whose units, dealt heaviest
+// first onto kCUs workgroup slots (one resident unit per CU), finish within 2%
+// of the ideal time, else the best one. Units are costed with the causal
+// square mask whatever the call's mask, so that the workspace size (asked
+// without the mask) and the launch agree. Block calls keep the simpler rule of
+// enough units (their workspace is sized once for every offset).
+constexpr int kCUs = 256;
+constexpr long long kSimUnits = 1 << 14;  // beyond this many units the deal is balanced anyway
+
+double deal_efficiency(const AttnShape& sh, int ns) {
+  const int g = sh.Hq / sh.Hkv, hps = g / ns;
+  const int NT = (sh.Sk + kKBC - 1) / kKBC, NQ = (sh.Sq + kKBR - 1) / kKBR;
+  const long long streams = (long long)sh.B * sh.Hkv * ns;
+  if (streams * NT >= kSimUnits) return 1.0;
+  std::priority_queue<long long, std::vector<long long>, std::greater<long long>> load;
+  for (int c = 0; c < kCUs; ++c) load.push(0);
+  long long total = 0;
+  for (int jt = 0; jt < NT; ++jt) {           // key tile 0 is the heaviest under the causal mask
+    const int i_min = (jt * kKBC) / kKBR;
+    const long long cost = (long long)std::max(0, NQ - i_min) * hps + 2;  // + loads and epilogue
+    for (long long u = 0; u < streams; ++u) {
+      const long long t = load.top();
+      load.pop();
+      load.push(t + cost);
+      total += cost;
+    }
   }
-  return ns;
+  long long makespan = 0;
+  while (!load.empty()) {
+    makespan = std::max(makespan, load.top());
+    load.pop();
+  }
+  return makespan ? (double)total / kCUs / makespan : 1.0;
+}
+
+int choose_head_split(const AttnShape& sh, bool block) {
+  const int g = sh.Hq / sh.Hkv;
+  if (block) {
+    const long long units = (long long)sh.B * sh.Hkv * ((sh.Sk + kKBC - 1) / kKBC);
+    int ns = 1;
+    while (units * ns < kTargetUnits && ns < g) {
+      int next = ns + 1;
+      while (g % next) ++next;
+      ns = next;
+    }
+    return ns;
+  }
+  AttnShape sq = sh;
+  sq.Sq = sq.Sk = std::max(sh.Sq, sh.Sk);
+  int best = 1;
+  double best_eff = -1.0;
+  for (int ns = 1; ns <= g; ++ns) {
+    if (g % ns) continue;
+    const double eff = deal_efficiency(sq, ns);
+    if (eff >= 0.98) return ns;
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = ns;
+    }
+  }
+  return best;
 }
 
 struct WsLayout {
@@ -81,7 +140,7 @@ struct WsLayout {
 WsLayout ws_layout(const AttnShape& sh, bool block = false) {
   WsLayout w;
   const size_t rows = (size_t)sh.B * sh.Hq * sh.Sq;
-  w.nsplit = choose_head_split(sh);
+  w.nsplit = choose_head_split(sh, block);
   w.delta = 0;
   w.lse2 = align256(rows * 4);
   size_t off = w.lse2 + align256(rows * 4);

@@ -215,6 +215,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
         s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + kb * 32 * T::ROW_BYTES + koff[ks]), qf[ks], s[kb]);
+    if (NKB == 2) {
+      // keep three operand pairs in flight: six K reads first, then two
+      // products per two reads (left alone, the scheduler reads each pair
+      // just before its products and waits out every LDS round trip)
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // LDS reads
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    }
 
     // Whether this row may see the key of accumulator element v of block kb:
     // that key is kv0 + 32 KB0 + 4half + off with the constant
