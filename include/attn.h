@@ -116,8 +116,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * attn_bwd for measurement tools: identical arguments, results and errors,
  * plus ATTN_BWD_EVENTS caller-created events (hipEventCreate) recorded on
  * `stream` around the backward kernels:
- *   events[0] before the row-term pass (Delta from the stored O, scaled LSE)
- *   events[1] after it, before the dQ kernel
+ *   events[0], events[1] before the dQ kernel, back to back (the row terms,
+ *             Delta from the stored O and the scaled LSE, are formed inside
+ *             the dQ kernel; the slot is kept so the layout stays the same)
  *   events[2] after the dQ kernel, before the dK/dV kernel
  *   events[3] after the dK/dV kernel
  *   events[4] after the fixed-order sum of per-head-subset dK/dV partials

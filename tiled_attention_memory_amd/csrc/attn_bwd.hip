@@ -11,7 +11,10 @@
 //
 // Kernels, all on the caller's stream:
 //   1. prep:  Delta~ = sum_d dO_id O_id from the stored bf16 O, and
-//             LSE * log2(e), per query row (workspace).
+//             LSE * log2(e), per query row (workspace). Only the block
+//             protocol runs it as a kernel of its own; on the whole-sequence
+//             path the dQ kernel forms both for its rows (its dS wave holds
+//             the row's dO already) and stores lse2 for kernel 3.
 //   2. dq:    query-stationary, like the forward pass: dQ^T += K^T dS^T, with
 //             the same wave-pair split as kernel 3 (one wave computes S, P and
 //             P K, its partner dP, dS and dQ one key tile behind). It also
@@ -625,8 +628,12 @@ struct DqArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  float* delta;  // in: Delta~ from the stored O; out: exact Delta (final mode)
-  const float* lse2;
+  float* delta;  // in: Delta~ from the stored O (unless o is set); out: exact Delta (final mode)
+  float* lse2;   // in: LSE * log2(e) (unless o is set); out: the same, when o is set
+  // Whole-sequence calls set o and lse: the kernel then forms Delta~ = sum_d dO O
+  // and lse2 itself instead of reading them from the workspace.
+  const uint16_t* o;
+  const float* lse;
   uint16_t* dq;  // final mode: dQ = scale (sum dS~ K - c P K)
   // Accumulate mode (all three set, dq unused): this call's key block adds its
   // sum dS~ K, P K and c = sum dS~ to these fp32 buffers ([rows, D], [rows, D],
@@ -697,7 +704,33 @@ void attn_bwd_dq_kernel(DqArgs a) {
       xf[ks] = qrow < Sq ? *reinterpret_cast<const bf16x8*>(src + 16 * ks)
                         : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
   }
-  const float rowval = qrow < Sq ? (prole ? a.lse2 : a.delta)[(size_t)bh * Sq + qrow] : 0.f;  // lse2 or Delta~
+  // lse2 (P role) or Delta~ (dS role) of this lane's row
+  float rowval = 0.f;
+  if (qrow < Sq) {
+    const size_t r = (size_t)bh * Sq + qrow;
+    if (!a.o) {
+      rowval = (prole ? a.lse2 : a.delta)[r];
+    } else if (prole) {
+      // a row that sees no key has LSE = -inf; +inf makes all its probabilities 0
+      const float l = a.lse[r];
+      rowval = l == -INFINITY ? INFINITY : l * kLog2e;
+      if (half == 0) a.lse2[r] = rowval;   // for the dK/dV kernel
+    } else {
+      // this lane's half of Delta~ = sum_d dO_d O_d: head-dim entries 16 ks + 8 half + (0..7)
+      const uint16_t* op = a.o + q_base + (size_t)qrow * D + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 ov = *reinterpret_cast<const u32x4*>(op + 16 * ks);
+        const u32x4 dv = __builtin_bit_cast(u32x4, xf[ks]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          rowval = fmaf(bf16_lo(ov[w]), bf16_lo(dv[w]), rowval);
+          rowval = fmaf(bf16_hi(ov[w]), bf16_hi(dv[w]), rowval);
+        }
+      }
+    }
+  }
+  if (a.o && !prole) rowval = sum_halves(rowval);  // every lane takes part in the exchange
 
   // Per-lane LDS offsets (see SwzTile) into the stage this wave reads next:
   // roff for the key-by-row products (K for the P role, V for the dS role),
@@ -1063,7 +1096,8 @@ hipError_t launch_fill_zero(float* p, long long n, hipStream_t stream) {
 // dQ kernel: final mode (dq set) or accumulate mode (dq null).
 template <int D, bool CAUSAL>
 hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                     const uint16_t* dout, uint16_t* dq, const Ws& ws, hipStream_t stream) {
+                     const uint16_t* dout, uint16_t* dq, const Ws& ws, hipStream_t stream,
+                     const uint16_t* o = nullptr, const float* lse = nullptr) {
   DqArgs a;
   a.q = q;
   a.k = k;
@@ -1071,6 +1105,8 @@ hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, 
   a.dout = dout;
   a.delta = ws.delta;
   a.lse2 = ws.lse2;
+  a.o = o;
+  a.lse = lse;
   a.dq = dq;
   a.acc_dq = dq ? nullptr : ws.acc_dq;
   a.acc_pk = dq ? nullptr : ws.acc_pk;
@@ -1145,10 +1181,12 @@ hipError_t launch_all(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
   hipError_t e;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return e;
-  // 1. Delta~ and lse2
-  if ((e = launch_prep<D>(sh, o, dout, lse, ws, stream)) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
-  // 2. dQ (also turns Delta~ into the exact Delta)
-  if ((e = launch_dq<D, CAUSAL>(sh, q, k, v, dout, dq, ws, stream)) != hipSuccess || (e = mark(2)) != hipSuccess)
+  // 1. (Delta~ and lse2 are formed inside the dQ kernel on this path; the
+  //    event slot is kept so the per-kernel timing layout stays the same)
+  if ((e = mark(1)) != hipSuccess) return e;
+  // 2. dQ, which also writes lse2 and the exact Delta for the dK/dV kernel
+  if ((e = launch_dq<D, CAUSAL>(sh, q, k, v, dout, dq, ws, stream, o, lse)) != hipSuccess ||
+      (e = mark(2)) != hipSuccess)
     return e;
   // 3. dK/dV
   if ((e = launch_dkdv<D, CAUSAL>(sh, q, k, v, dout, dk, dv, ws, stream)) != hipSuccess ||
