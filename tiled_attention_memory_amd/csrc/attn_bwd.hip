@@ -431,14 +431,19 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
     for (int qs = 0; qs < 2; ++qs) {
       const bool run = runs(masked, it, qs);
       float p[16];
+      // Dropout bytes: the four lanes of a quad hold keys 4m .. 4m + 3 and need
+      // the same four generator calls (row groups i = 0..3); lane 4m + j makes
+      // call j, turns its words so that word n holds key n's bytes of rows
+      // 0..3, and the quad swaps: dq4[i] then has byte r = row 8i + 4half + r
+      // of this lane's key.
+      u32x4 dq4 = {0u, 0u, 0u, 0u};
+      if (DROP)
+        dq4 = quad_transpose(byte_transpose(philox4x32_10(
+            (uint32_t)kvrow >> 2, (uint32_t)(it * kKBR + qs * 32 + 8 * (lane & 3) + 4 * half) >> 2, bhq, 0u,
+            a.drop.seed_lo, a.drop.seed_hi)));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x4 l2 = *reinterpret_cast<const f32x4*>(Fs + qs * 32 + 8 * i + 4 * half);
-        // dropout bytes of rows R .. R + 3 (word r) for this lane's key (byte kvrow % 4)
-        u32x4 dw = {0u, 0u, 0u, 0u};
-        if (DROP)
-          dw = philox4x32_10((uint32_t)kvrow >> 2, (uint32_t)(it * kKBR + qs * 32 + 8 * i + 4 * half) >> 2, bhq, 0u,
-                             a.drop.seed_lo, a.drop.seed_hi);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * i + r;
@@ -450,7 +455,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
             e = ok ? e : 0.f;
           }
           if (DROP) {
-            const bool keep = drop_keep(dw[r], kvrow & 3, a.drop.t);
+            const bool keep = drop_keep(dq4[i], r, a.drop.t);
             pb[(16 * qs + v) * 64] = keep ? e : -e;
             p[v] = keep ? e * a.drop.r : 0.f;
           } else {
@@ -833,7 +838,15 @@ void attn_bwd_dq_kernel(DqArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float pf[16];
-      uint32_t dbytes = 0u;
+      // Dropout words: the four lanes of a quad hold rows 4m .. 4m + 3 and need
+      // the same four generator calls (key groups of this half); lane 4m + j
+      // makes call j and the quad swaps, leaving each lane its row's word of
+      // every call (dwords[i] for keys kv0 + 32kb + 8i + 4half + 0..3).
+      u32x4 dwords = {0u, 0u, 0u, 0u};
+      if (DROP)
+        dwords = quad_transpose(philox4x32_10((uint32_t)(kv0 + kb * 32 + 8 * (lane & 3) + 4 * half) >> 2,
+                                              (uint32_t)qrow >> 2, (uint32_t)bh, 0u, a.drop.seed_lo,
+                                              a.drop.seed_hi));
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float e = fast_exp2(fmaf(x[kb][v], c, -rowval));
@@ -844,10 +857,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
         }
         pf[v] = e;
         if (DROP) {
-          if ((v & 3) == 0)
-            dbytes = drop_row_bytes(a.drop, (uint32_t)bh, (uint32_t)qrow,
-                                    (uint32_t)(kv0 + kb * 32 + 8 * (v >> 2) + 4 * half) >> 2);
-          pb[(16 * kb + v) * 64] = drop_keep(dbytes, v & 3, a.drop.t) ? e : -e;
+          pb[(16 * kb + v) * 64] = drop_keep(dwords[v >> 2], v & 3, a.drop.t) ? e : -e;
         } else {
           pb[(16 * kb + v) * 64] = e;
         }

@@ -270,16 +270,48 @@ __host__ inline DropParams make_drop(int t, unsigned long long seed) {
   return d;
 }
 
-// The 4 bytes of row i for keys 4 * k4 .. 4 * k4 + 3 (byte n for key 4 k4 + n).
-__device__ __forceinline__ uint32_t drop_row_bytes(const DropParams& d, uint32_t bhq, uint32_t i, uint32_t k4) {
-  const u32x4 w = philox4x32_10(k4, i >> 2, bhq, 0u, d.seed_lo, d.seed_hi);
-  const uint32_t s = i & 3u;
-  return s == 0 ? w[0] : s == 1 ? w[1] : s == 2 ? w[2] : w[3];
-}
-
 // Whether byte n (0..3) of a word of drop bytes keeps its pair.
 __device__ __forceinline__ bool drop_keep(uint32_t bytes, int n, uint32_t t) {
   return ((bytes >> (8 * n)) & 0xFFu) >= t;
+}
+
+// 4 x 4 transpose across each quad of lanes (4m .. 4m + 3): on return,
+// element i of lane 4m + j holds what element j of lane 4m + i held. Two
+// butterfly steps (partner lane xor 1, then xor 2) with DPP quad permutes.
+// Every lane of the quad must be active. Used to share generator calls: four
+// neighbouring lanes that need the same four calls each make one and swap.
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 w) {
+  const int q = (int)(__lane_id() & 3u);
+#pragma unroll
+  for (int k = 0; k < 4; k += 2) {   // partner lane ^ 1, elements k and k + 1
+    const uint32_t send = (q & 1) ? w[k] : w[k + 1];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    if (q & 1)
+      w[k] = recv;
+    else
+      w[k + 1] = recv;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {      // partner lane ^ 2, elements k and k + 2
+    const uint32_t send = (q & 2) ? w[k] : w[k + 2];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    if (q & 2)
+      w[k] = recv;
+    else
+      w[k + 2] = recv;
+  }
+  return w;
+}
+
+// 4 x 4 transpose of the bytes of four words: byte r of word n of the result
+// is byte n of word r of the input.
+__device__ __forceinline__ u32x4 byte_transpose(u32x4 w) {
+  const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.b0 w1.b0 w0.b1 w1.b1
+  const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.b2 w1.b2 w0.b3 w1.b3
+  const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+  const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+  return u32x4{__builtin_amdgcn_perm(lo23, lo01, 0x05040100u), __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+               __builtin_amdgcn_perm(hi23, hi01, 0x05040100u), __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
 }
 
 // Rotary position embedding (rotate-half pairing): the pair (x_d, x_{d+D/2})

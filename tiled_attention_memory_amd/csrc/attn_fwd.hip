@@ -279,15 +279,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       // the row sum above is taken before dropout; the product with V uses
       // the kept probabilities scaled by r
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb) {
+        // The four lanes of a quad hold rows 4m .. 4m + 3 and need the same
+        // four generator calls (key groups i = 0..3 of this half): lane 4m + j
+        // makes call j and the quad swaps, leaving each lane its row's word of
+        // every call.
+        const uint32_t k4 = (uint32_t)(kv0 + 32 * (KB0 + kb) + 8 * (lane & 3) + 4 * half) >> 2;
+        const u32x4 words = quad_transpose(
+            philox4x32_10(k4, (uint32_t)tok >> 2, (uint32_t)bh, 0u, a.drop.seed_lo, a.drop.seed_hi));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t k4 = (uint32_t)(kv0 + 32 * (KB0 + kb) + 8 * i + 4 * half) >> 2;
-          const uint32_t bytes = drop_row_bytes(a.drop, (uint32_t)bh, (uint32_t)tok, k4);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4)
-            p[kb][4 * i + r4] = drop_keep(bytes, r4, a.drop.t) ? p[kb][4 * i + r4] * a.drop.r : 0.f;
-        }
+            p[kb][4 * i + r4] = drop_keep(words[i], r4, a.drop.t) ? p[kb][4 * i + r4] * a.drop.r : 0.f;
+      }
     }
 
     bf16x8 pb[NKB][2];
