@@ -324,8 +324,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 
   // Tile j on stage cur while tile j + 1 loads into nxt; one barrier per tile
   // for every wave, whichever loop below runs it.
-  // a wave whose rows are all padding (packed rows fewer than 128) only loads
-  const bool wave_rows = !packed || wave * 32 < a.pack * Sq;
+  // a wave whose rows are all padding (packed rows fewer than 128, or a
+  // sequence that ends before the wave's first row) only loads
+  const bool wave_rows = packed ? wave * 32 < a.pack * Sq : w_tmin < Sq;
   auto step = [&](auto masked_tag, int j, const unsigned char* cur, unsigned char* nxt) TAM_INLINE {
     if (j + 1 < jend) issue(j + 1, nxt);
     if (wave_rows)
