@@ -198,7 +198,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   // so scores of hidden keys are excluded; such tiles run one 32-key block at
   // a time, which keeps fewer scores live. Every other tile runs both blocks
   // without any per-element test.
-  auto tile = [&](auto masked_tag, auto kb0_tag, auto nkb_tag, int kv0, const unsigned char* cur) TAM_INLINE {
+  auto tile = [&](auto masked_tag, auto kb0_tag, auto nkb_tag, int kv0, const unsigned char* cur,
+                  auto&& after_scores) TAM_INLINE {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int KB0 = decltype(kb0_tag)::value;
     constexpr int NKB = decltype(nkb_tag)::value;
@@ -239,6 +240,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[kb][v] = visible(kb, v) ? s[kb][v] : -INFINITY;
     }
+    after_scores();   // e.g. the next tile's loads, issued while the products run
     float ext = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -328,9 +330,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   // sequence that ends before the wave's first row) only loads
   const bool wave_rows = packed ? wave * 32 < a.pack * Sq : w_tmin < Sq;
   auto step = [&](auto masked_tag, int j, const unsigned char* cur, unsigned char* nxt) TAM_INLINE {
-    if (j + 1 < jend) issue(j + 1, nxt);
+    // the next tile's loads go out once this tile's score products are queued
+    auto next = [&]() TAM_INLINE {
+      if (j + 1 < jend) issue(j + 1, nxt);
+    };
     if (wave_rows)
-      tile(masked_tag, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, j * kBC, cur);
+      tile(masked_tag, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, j * kBC, cur, next);
+    else
+      next();
     wait_loads();
     __syncthreads();
   };
@@ -359,12 +366,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     using C1 = std::integral_constant<int, 1>;
     using C2 = std::integral_constant<int, 2>;
     if (wave_rows && (!CAUSAL || kv0 <= w_tmax + dlt)) {   // some key of the tile is visible to this wave
+      auto nothing = []() TAM_INLINE {};
       if (jj < jplain) {
-        tile(std::false_type{}, C0{}, C2{}, kv0, cur);
+        tile(std::false_type{}, C0{}, C2{}, kv0, cur, nothing);
       } else {
-        tile(std::true_type{}, C0{}, C1{}, kv0, cur);
+        tile(std::true_type{}, C0{}, C1{}, kv0, cur, nothing);
         // the second 32-key block, unless this wave sees none of its keys
-        if ((!CAUSAL || kv0 + 32 <= w_tmax + dlt) && kv0 + 32 < kend) tile(std::true_type{}, C1{}, C1{}, kv0, cur);
+        if ((!CAUSAL || kv0 + 32 <= w_tmax + dlt) && kv0 + 32 < kend)
+          tile(std::true_type{}, C1{}, C1{}, kv0, cur, nothing);
       }
     }
     wait_loads();
