@@ -509,12 +509,12 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
     advance(nxt);
     if (vrole) {
       for (int st = 0; st < nsteps; ++st) {
-        if (st + 1 < nsteps) issue(st + 1, nxt);
         const int it = cur.it;
         const bool masked = masked_at(it);
         const uint32_t bhq = (uint32_t)(b * a.Hq + cur.h);
         f32x16 x[2];
         rows_by_keys_at(masked, it, x);
+        if (st + 1 < nsteps) issue(st + 1, nxt);  // after the score products: the issue stalls overlap them
         bf16x8 hi[2][2], lo[2][2];
         if (masked)
           probabilities(std::true_type{}, st, it, bhq, masked, x, hi, lo);
