@@ -26,3 +26,35 @@ def test_scheduler(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     print(out.stdout)
     assert out.returncode == 0, out.stdout + out.stderr
+
+
+def _head_split(B, Hq, Hkv, S, D):
+    """Head subsets the dK/dV kernel uses for a whole-sequence call, read off the workspace size
+    (two fp32 rows of B*Hq*S, each padded to 256 bytes, then nsplit x 2 partial copies of dK/dV
+    when nsplit > 1)."""
+    import tiled_attention_memory_amd as tam
+    ws = tam.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)
+    pad = lambda n: (n + 255) // 256 * 256
+    base = 2 * pad(B * Hq * S * 4)
+    if ws == base:
+        return 1
+    part = 2 * B * Hkv * S * D * 4
+    assert (ws - base) % part == 0, (ws, base, part)
+    return (ws - base) // part
+
+
+def test_dkdv_head_split_follows_balance():
+    # The split is the smallest divisor of g whose units, dealt heaviest first over 256 CUs, come
+    # within 2% of the ideal time: the Llama-2-70B layer (256 units at n = 1, heaviest unit twice
+    # the mean) needs 2, S = 32768 has 2048 units at n = 1, S = 81920 (640 units) needs 4, the
+    # batch-16 x 64 shape (128 units of one tile) needs 2.
+    from tiled_attention_memory_amd import workloads as wl
+    want = {"smoke_s256_d64": 1, "llama2_70b_layer_s4096": 2, "llama3_405b_lora_b16_s64": 2,
+            "long_context_s32768_k3": 1, "very_long_s81920": 4}
+    for name, n in want.items():
+        w = wl.BY_NAME[name]
+        assert _head_split(w.B, w.Hq, w.Hkv, w.S, w.D) == n, name
+    # a group of one query head cannot be split
+    assert _head_split(1, 8, 8, 64, 128) == 1
+    # more heads per group never shrinks the subsets below one head
+    assert 16 % _head_split(1, 16, 1, 128, 128) == 0
