@@ -284,11 +284,13 @@ def decode_bench(args, w):
     import tiled_attention_memory_amd as tam
     from tiled_attention_memory_amd import workloads as wl
     B, Sq, Sk = (int(t) for t in args.decode.split(","))
-    x = wl.make_inputs(B, w.Hq, w.Hkv, Sk, w.D, seed=(500, B, Sq, Sk))
+    # the cache (Sk keys and values) and the Sq new tokens' queries
+    x = wl.make_inputs(B, w.Hq, w.Hkv, Sk, w.D, seed=(500, B, Sq, Sk), tensors=("k", "v"))
+    x.update(wl.make_inputs(B, w.Hq, w.Hkv, Sq, w.D, seed=(501, B, Sq, Sk), tensors=("q",)))
     dev = {n: torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(torch.bfloat16).cuda()
            for n in ("q", "k", "v")}
-    q = dev["q"][:, :, Sk - Sq:].contiguous()
-    k, v = dev["k"], dev["v"]
+    del x
+    q, k, v = dev["q"], dev["k"], dev["v"]
     del dev
     o = torch.empty_like(q)
     lse = torch.empty((B, w.Hq, Sq), dtype=torch.float32, device="cuda")
@@ -302,9 +304,16 @@ def decode_bench(args, w):
     torch.cuda.synchronize()
     K = args.steps
     evs = [(hip.event(), hip.event()) for _ in range(K)]
+    if flush is not None:
+        flush.fill_(1.0)
     for i in range(K):
         if flush is not None:
-            flush.fill_(float(i))
+            # reading evicts the cache without leaving dirty lines whose write-back
+            # would compete with the timed call; --flush-mode write measures that case
+            if args.flush_mode == "write":
+                flush.fill_(float(i))
+            else:
+                flush.sum()
         hip.record(evs[i][0], sh)
         tam.attn_decode(q, k, v, o, lse, ws, causal=True, scale=w.scale)
         hip.record(evs[i][1], sh)
@@ -323,7 +332,8 @@ def decode_bench(args, w):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"decode_b{B}_q{Sq}_s{Sk}_h{w.Hq}x{w.Hkv}_d{w.D}", "B": B, "Hq": w.Hq,
                    "Hkv": w.Hkv, "Sq": Sq, "Sk": Sk, "D": w.D, "causal": True,
-                   "cache": "cold" if flush is not None else "warm"},
+                   "cache": ("warm" if flush is None else "cold" if args.flush_mode == "read"
+                             else "cold, after a write")},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": None},
     }
@@ -354,6 +364,10 @@ def main():
                     help="before each step, overwrite a MIB-mebibyte buffer so that L2 and the "
                          "memory-side cache start cold (for the short, bandwidth-bound shapes); "
                          "the step time is then the sum of the per-kernel event times")
+    ap.add_argument("--flush-mode", choices=("read", "write"), default="read",
+                    help="with --decode and --flush-mib: evict the cache by reading the buffer "
+                         "(default) or by overwriting it, which leaves dirty lines whose write-back "
+                         "overlaps the timed call")
     ap.add_argument("--cpu-groups", type=int, default=8)
     ap.add_argument("--hbm-probe", type=int, default=0, metavar="MIB",
                     help="instead of attention: achievable HBM bandwidth of plain library kernels "

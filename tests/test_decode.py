@@ -40,6 +40,9 @@ CASES = [
     (3, 16, 1, 8, 777, 64, True),       # 16 x 8 = 128 rows (the limit), D = 64
     (1, 4, 4, 5, 5, 128, True),         # the whole sequence is new
     (2, 8, 2, 3, 2048, 128, False),
+    (32, 16, 8, 1, 300, 64, True),      # 256 groups: one key split, output written directly
+    (1, 16, 1, 8, 1500, 128, True),     # 128 rows at D = 128: one 32-row block per wave
+    (1, 8, 1, 10, 900, 128, False),     # 80 rows: three row blocks, the fourth wave only loads
 ]
 
 

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libattn.so")
-SOURCES = ["attn_abi.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_merge.hip", "attn_rope.hip"]
+SOURCES = ["attn_abi.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_merge.hip", "attn_rope.hip",
+           "attn_decode.hip"]
 
 
 def hipcc() -> str:

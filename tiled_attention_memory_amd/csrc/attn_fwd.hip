@@ -47,13 +47,6 @@ struct FwdArgs {
   float* lse;
   int Hq, Hkv, Sq, Sk, dlt;
   float c;  // softmax scale * log2(e): scores are exponentiated in base 2
-  // Packed rows (decode): pack > 0 is the group size g, a unit holds the Sq
-  // tokens of all g query heads of one kv head (row r = head r / Sq, token
-  // r % Sq; g * Sq <= 128), its tile index is a split of the keys into chunks
-  // of kv_chunk, and split s writes its fp32 partials at o32 + s * o_stride and
-  // lse + s * lse_stride.
-  int pack, kv_chunk;
-  long long o_stride, lse_stride;
   DropParams drop;  // dropout on the probabilities (DROP kernels only)
   const float2* rope;  // (cos, sin) table [Sq][D/2]: rotate the Q rows at load; null = none
   TileSched sched;
@@ -85,36 +78,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
   const int col = lane & 31, half = lane >> 5;
   const int Sq = a.Sq, Sk = a.Sk, dlt = a.dlt;
-  const bool packed = a.pack > 0;
-  const int r = wave * 32 + col;     // the row of the unit this lane owns
-  int b, kvh, tok, w_tmin, w_tmax, t_last, kbeg, kend, split = 0;
-  bool row_ok;
-  size_t row_off;                    // element offset of this lane's row in q, o (and / D in lse)
-  if (packed) {                      // unit = (batch, kv head, key split)
-    b = bh / a.Hkv;
-    kvh = bh - b * a.Hkv;
-    split = qt;
-    const int hoff = r / Sq;
-    tok = r - hoff * Sq;
-    row_ok = hoff < a.pack;
-    row_off = ((size_t)(b * a.Hq + kvh * a.pack + hoff) * Sq + tok) * D;
-    w_tmin = 0;
-    w_tmax = Sq - 1;
-    t_last = Sq - 1;
-    kbeg = split * a.kv_chunk;
-    kend = min(Sk, kbeg + a.kv_chunk);
-  } else {                           // unit = (batch, query head, 128-row tile)
-    b = bh / a.Hq;
-    kvh = (bh - b * a.Hq) / (a.Hq / a.Hkv);
-    tok = qt * kBR + r;
-    row_ok = tok < Sq;
-    row_off = ((size_t)bh * Sq + tok) * D;
-    w_tmin = qt * kBR + wave * 32;   // the wave's first row
-    w_tmax = w_tmin + 31;
-    t_last = min(qt * kBR + kBR, Sq) - 1;
-    kbeg = 0;
-    kend = Sk;
-  }
+  // unit = (batch, query head, 128-row tile)
+  const int b = bh / a.Hq;
+  const int kvh = (bh - b * a.Hq) / (a.Hq / a.Hkv);
+  const int tok = qt * kBR + wave * 32 + col;  // the query row this lane owns
+  const bool row_ok = tok < Sq;
+  const size_t row_off = ((size_t)bh * Sq + tok) * D;  // element offset of the row in q, o (and / D in lse)
+  const int w_tmin = qt * kBR + wave * 32;     // the wave's first row
+  const int w_tmax = w_tmin + 31;
+  const int t_last = min(qt * kBR + kBR, Sq) - 1;
+  constexpr int kbeg = 0;                      // the unit's keys: all of them
+  const int kend = Sk;
   const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)Sk * D;
   const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)Sk * D;
 
@@ -167,8 +141,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NLD; ++i) loff[i] = T::load_src(wave * NLD + i, lane);
 
-  // key tiles [jbeg, jend) of the unit's key range; the last key any row of
-  // the unit may see is t_last + dlt
+  // key tiles [jbeg, jend); the last key any row of the unit may see is t_last + dlt
   const int jbeg = kbeg / kBC;
   const int n_kv = (kend + kBC - 1) / kBC;
   const int jend = CAUSAL ? (t_last + dlt < kbeg ? jbeg : min(n_kv, (t_last + dlt) / kBC + 1)) : n_kv;
@@ -326,20 +299,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 
   // Tile j on stage cur while tile j + 1 loads into nxt; one barrier per tile
   // for every wave, whichever loop below runs it.
-  // a wave whose rows are all padding (packed rows fewer than 128, or a
-  // sequence that ends before the wave's first row) only loads
-  const bool wave_rows = packed ? wave * 32 < a.pack * Sq : w_tmin < Sq;
   auto step = [&](auto masked_tag, int j, const unsigned char* cur, unsigned char* nxt) TAM_INLINE {
     // the next tile's loads go out once this tile's score products are queued
     auto next = [&]() TAM_INLINE {
       if (j + 1 < jend) issue(j + 1, nxt);
     };
-    if (wave_rows)
-      tile(masked_tag, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, j * kBC, cur, next);
-    else
-      next();
+    tile(masked_tag, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{}, j * kBC, cur, next);
+    // each tile is its own scheduling region: products moved across the
+    // barrier would wait for the other waves or break up the next tile's
+    // read-ahead pattern
+    __builtin_amdgcn_sched_barrier(0);
     wait_loads();
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Leading tiles lie entirely below this wave's diagonal and inside the
@@ -349,6 +321,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   if (jend > jbeg) issue(jbeg, stage0);
   wait_loads();
   __syncthreads();
+  if (w_tmin >= Sq) {
+    // a wave whose rows all lie past the end of the sequence only loads its
+    // share of each tile and meets the others at every barrier (its own loop
+    // keeps that test out of the loops below)
+    for (int jj = jbeg; jj < jend; ++jj) {
+      if (jj + 1 < jend) issue(jj + 1, (jj - jbeg) & 1 ? stage0 : stage1);
+      wait_loads();
+      __syncthreads();
+    }
+    return;
+  }
   int j = jbeg;
   for (; j + 2 <= jplain; j += 2) {
     step(std::false_type{}, j, stage0, stage1);
@@ -365,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
     using C2 = std::integral_constant<int, 2>;
-    if (wave_rows && (!CAUSAL || kv0 <= w_tmax + dlt)) {   // some key of the tile is visible to this wave
+    if (!CAUSAL || kv0 <= w_tmax + dlt) {   // some key of the tile is visible to this wave
       auto nothing = []() TAM_INLINE {};
       if (jj < jplain) {
         tile(std::false_type{}, C0{}, C2{}, kv0, cur, nothing);
@@ -392,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     const bool seen = l_tot > 0.f;
     const float inv = seen ? 1.f / l_tot : 0.f;
     if (a.o32) {
-      float* op = a.o32 + split * a.o_stride + row_off + 4 * half;
+      float* op = a.o32 + row_off + 4 * half;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -417,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
           *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
         }
     }
-    if (half == 0) a.lse[split * a.lse_stride + row_off / D] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (half == 0) a.lse[row_off / D] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -436,9 +419,6 @@ hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, con
   a.Sq = sh.Sq;
   a.Sk = sh.Sk;
   a.dlt = sh.dlt;
-  a.pack = 0;
-  a.kv_chunk = 0;
-  a.o_stride = a.lse_stride = 0;
   a.drop = make_drop(sh.drop_t, sh.seed);
   a.rope = sh.rope;
   a.c = sh.scale * kLog2e;
@@ -452,72 +432,7 @@ hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, con
   return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_decode_t(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                           uint16_t* o, float* lse, void* workspace, hipStream_t stream) {
-  const DecodePlan p = decode_plan(sh);
-  const long long rows = (long long)sh.B * sh.Hq * sh.Sq;
-  float* parts = static_cast<float*>(workspace);
-  float* lparts = parts + (size_t)p.splits * rows * sh.D;
-  FwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = nullptr;
-  a.o32 = parts;
-  a.lse = lparts;
-  a.Hq = sh.Hq;
-  a.Hkv = sh.Hkv;
-  a.Sq = sh.Sq;
-  a.Sk = sh.Sk;
-  a.dlt = sh.dlt;
-  a.pack = sh.Hq / sh.Hkv;
-  a.kv_chunk = p.chunk;
-  a.o_stride = rows * sh.D;
-  a.lse_stride = rows;
-  a.drop = DropParams{0u, 0u, 0u, 1.f};
-  a.rope = nullptr;
-  a.c = sh.scale * kLog2e;
-  a.sched.BH = sh.B * sh.Hkv;
-  a.sched.NT = p.splits;
-  a.sched.chunk = (a.sched.BH + 7) / 8;
-  void* args[] = {&a};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL>),
-                                 dim3((unsigned)sched_grid(a.sched)), dim3(kThreads), args, 0, stream);
-  if (e != hipSuccess) return e;
-  return launch_merge_strided(parts, lparts, p.splits, rows * sh.D, rows, o, lse, rows, sh.D, stream);
-}
-
 }  // namespace
-
-// Decode splits: enough (kv head, split) units to give every CU two
-// workgroups, but no split shorter than 256 keys.
-DecodePlan decode_plan(const AttnShape& sh) {
-  const long long units = (long long)sh.B * sh.Hkv;
-  long long want = (512 + units - 1) / units;
-  const long long by_keys = (sh.Sk + 255) / 256;
-  if (want > by_keys) want = by_keys;
-  if (want < 1) want = 1;
-  const int chunk = (int)(((sh.Sk + want - 1) / want + kBC - 1) / kBC * kBC);
-  DecodePlan p;
-  p.chunk = chunk;
-  p.splits = (sh.Sk + chunk - 1) / chunk;
-  return p;
-}
-
-size_t decode_workspace_bytes(const AttnShape& sh) {
-  const DecodePlan p = decode_plan(sh);
-  const size_t rows = (size_t)sh.B * sh.Hq * sh.Sq;
-  return (size_t)p.splits * rows * (sh.D + 1) * 4;
-}
-
-hipError_t launch_decode(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                         float* lse, void* workspace, hipStream_t stream) {
-  if (sh.D == 128) return sh.causal ? launch_decode_t<128, true>(sh, q, k, v, o, lse, workspace, stream)
-                                    : launch_decode_t<128, false>(sh, q, k, v, o, lse, workspace, stream);
-  return sh.causal ? launch_decode_t<64, true>(sh, q, k, v, o, lse, workspace, stream)
-                   : launch_decode_t<64, false>(sh, q, k, v, o, lse, workspace, stream);
-}
 
 hipError_t launch_fwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       uint16_t* o, float* o32, float* lse, hipStream_t stream) {

@@ -10,7 +10,7 @@
 // with parts whose LSE is -inf (rows that saw no key of that block) weighing 0
 // and a row that no block reaches left at O = 0, LSE = -inf.
 //
-// One pass over the rows, fp32 throughout, bf16 output: HBM-bound.
+// One pass over the parts, fp32 throughout, bf16 output: HBM-bound.
 #include <math.h>
 
 #include "attn_device.h"
@@ -33,23 +33,34 @@ struct MergeArgs {
   long long rows;
 };
 
+// Each row is handled by SG groups of D / 8 lanes, one wave or less: lane
+// group q takes parts q, q + SG, ... and the groups' maxima and weighted sums
+// are combined across lanes, so that rows with many parts (decode splits) do
+// not walk them one after another.
+constexpr int SG = 4;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(MergeArgs a) {
-  constexpr int TPR = D / 8;  // threads per row, 8 elements each
-  constexpr int RPB = kThreads / TPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  constexpr int TPR = D / 8;         // lanes per group, 8 elements each
+  constexpr int LPR = TPR * SG;      // lanes per row
+  constexpr int RPB = kThreads / LPR;
+  static_assert(LPR <= 64, "a row stays within one wave");
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
   const int part = threadIdx.x % TPR;
-  if (row >= a.rows) return;
-  float m = -INFINITY;
+  const int grp = (threadIdx.x / TPR) % SG;
+  if (row >= a.rows) return;         // whole rows, so whole lane groups, leave together
   auto lse_of = [&](int b) { return a.lse_base ? a.lse_base + b * a.lse_stride : a.lse[b]; };
   auto o_of = [&](int b) { return a.o_base ? a.o_base + b * a.o_stride : a.o[b]; };
-  for (int b = 0; b < a.n; ++b) m = fmaxf(m, lse_of(b)[row]);
+  float m = -INFINITY;
+  for (int b = grp; b < a.n; b += SG) m = fmaxf(m, lse_of(b)[row]);
+#pragma unroll
+  for (int x = TPR; x < LPR; x <<= 1) m = fmaxf(m, __shfl_xor(m, x));
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (m != -INFINITY) {
-    for (int b = 0; b < a.n; ++b) {
+    for (int b = grp; b < a.n; b += SG) {
       const float l = lse_of(b)[row];
-      if (l == -INFINITY) continue;
+      if (l == -INFINITY) continue;  // weighs 0, whatever its output holds
       const float w = expf(l - m);
       tot += w;
       const f32x4* src = reinterpret_cast<const f32x4*>(o_of(b) + row * D + part * 8);
@@ -57,6 +68,16 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(MergeArgs a) {
       acc1 += w * src[1];
     }
   }
+#pragma unroll
+  for (int x = TPR; x < LPR; x <<= 1) {
+    tot += __shfl_xor(tot, x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc0[i] += __shfl_xor(acc0[i], x);
+      acc1[i] += __shfl_xor(acc1[i], x);
+    }
+  }
+  if (grp != 0) return;
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
   u32x4 w = {pack_bf16(acc0[0] * inv, acc0[1] * inv), pack_bf16(acc0[2] * inv, acc0[3] * inv),
              pack_bf16(acc1[0] * inv, acc1[1] * inv), pack_bf16(acc1[2] * inv, acc1[3] * inv)};
@@ -68,7 +89,7 @@ hipError_t merge(MergeArgs& a, uint16_t* o, float* lse, long long rows, int D, h
   a.out = o;
   a.lse_out = lse;
   a.rows = rows;
-  const int rpb = kThreads / (D / 8);
+  const int rpb = kThreads / (D / 8 * SG);
   const long long grid = (rows + rpb - 1) / rpb;
   void* args[] = {&a};
   const void* k = D == 128 ? reinterpret_cast<const void*>(&attn_merge_kernel<128>)
