@@ -8,11 +8,13 @@
  * causal = 1 token t sees keys 0 .. Sk - Sq + t. The page "使用 PyTorch FSDP
  * 微調 Llama 2 70B" (agentlenshq.com), section "Flash Attention", splits the
  * scores into tiles combined by an online softmax; here the key range of each
- * (batch, kv head) is split into chunks processed in parallel, each giving a
- * partial output and log-sum-exp, and the chunks are merged exactly by their
- * log-sum-exps (the same combination as attn_merge in attn_block.h). The
- * query heads of a group share one pass over their cached keys and values,
- * which is what bounds this shape: every cached byte is read once.
+ * (batch, kv head) is split into chunks processed in parallel (as many as it
+ * takes to occupy every CU; none when there are enough (batch, kv head)
+ * pairs), each giving a partial output and log-sum-exp, and the chunks are
+ * merged exactly by their log-sum-exps (the same combination as attn_merge in
+ * attn_block.h). The query heads of a group share one pass over their cached
+ * keys and values, which is what bounds this shape: every cached byte is read
+ * once.
  *
  * Layout and rules as in attn.h: q, o bf16 [B, Hq, Sq, D]; k, v bf16
  * [B, Hkv, Sk, D]; lse f32 [B, Hq, Sq]; caller-owned, 16-byte aligned device
@@ -29,7 +31,8 @@
 extern "C" {
 #endif
 
-/* Bytes of device workspace attn_decode needs (fp32 partials of every chunk). */
+/* Bytes of device workspace attn_decode needs (fp32 partials of every chunk; a
+ * small minimum when the keys are not split). */
 int attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, size_t* bytes);
 
 /*

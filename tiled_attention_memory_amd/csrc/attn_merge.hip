@@ -49,33 +49,62 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(MergeArgs a) {
   const int part = threadIdx.x % TPR;
   const int grp = (threadIdx.x / TPR) % SG;
   if (row >= a.rows) return;         // whole rows, so whole lane groups, leave together
-  auto lse_of = [&](int b) { return a.lse_base ? a.lse_base + b * a.lse_stride : a.lse[b]; };
-  auto o_of = [&](int b) { return a.o_base ? a.o_base + b * a.o_stride : a.o[b]; };
-  float m = -INFINITY;
-  for (int b = grp; b < a.n; b += SG) m = fmaxf(m, lse_of(b)[row]);
-#pragma unroll
-  for (int x = TPR; x < LPR; x <<= 1) m = fmaxf(m, __shfl_xor(m, x));
+  // One pass with a running max: each lane group folds its parts into
+  // (m, tot, acc) relative to its largest LSE so far, loading four parts at a
+  // time before folding any of them, so that their loads are in flight together.
+  constexpr int U = 4;
+  float m = -INFINITY, tot = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  float tot = 0.f;
-  if (m != -INFINITY) {
-    for (int b = grp; b < a.n; b += SG) {
-      const float l = lse_of(b)[row];
-      if (l == -INFINITY) continue;  // weighs 0, whatever its output holds
-      const float w = expf(l - m);
-      tot += w;
-      const f32x4* src = reinterpret_cast<const f32x4*>(o_of(b) + row * D + part * 8);
-      acc0 += w * src[0];
-      acc1 += w * src[1];
+  auto fold = [&](auto lse_at, auto o_at) __attribute__((always_inline)) {
+    for (int b0 = grp; b0 < a.n; b0 += U * SG) {
+      float l[U];
+      f32x4 o0[U], o1[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int b = b0 + u * SG;
+        const int bl = b < a.n ? b : b0;  // past the last part: reload the first, weighed 0
+        const f32x4* src = o_at(bl);
+        l[u] = b < a.n ? lse_at(bl) : -INFINITY;
+        o0[u] = src[0];
+        o1[u] = src[1];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // a part with LSE = -inf weighs 0, whatever its output holds
+        const bool use = l[u] != -INFINITY;
+        const float mn = use ? fmaxf(m, l[u]) : m;
+        const float r = use ? expf(m - mn) : 1.f;  // 0 while nothing has been folded in (m = -inf)
+        const float w = use ? expf(l[u] - mn) : 0.f;
+        tot = tot * r + w;
+        acc0 = use ? acc0 * r + w * o0[u] : acc0;
+        acc1 = use ? acc1 * r + w * o1[u] : acc1;
+        m = mn;
+      }
     }
-  }
+  };
+  if (a.o_base)
+    fold([&](int b) { return a.lse_base[b * a.lse_stride + row]; },
+         [&](int b) { return reinterpret_cast<const f32x4*>(a.o_base + b * a.o_stride + row * D + part * 8); });
+  else
+    fold([&](int b) { return a.lse[b][row]; },
+         [&](int b) { return reinterpret_cast<const f32x4*>(a.o[b] + row * D + part * 8); });
+  // combine the row's lane groups
 #pragma unroll
   for (int x = TPR; x < LPR; x <<= 1) {
-    tot += __shfl_xor(tot, x);
+    const float mo = __shfl_xor(m, x), to = __shfl_xor(tot, x);
+    f32x4 b0, b1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc0[i] += __shfl_xor(acc0[i], x);
-      acc1[i] += __shfl_xor(acc1[i], x);
+      b0[i] = __shfl_xor(acc0[i], x);
+      b1[i] = __shfl_xor(acc1[i], x);
     }
+    const float mn = fmaxf(m, mo);
+    const float r = m == -INFINITY ? 0.f : expf(m - mn);
+    const float ro = mo == -INFINITY ? 0.f : expf(mo - mn);
+    tot = tot * r + to * ro;
+    acc0 = acc0 * r + b0 * ro;
+    acc1 = acc1 * r + b1 * ro;
+    m = mn;
   }
   if (grp != 0) return;
   const float inv = tot > 0.f ? 1.f / tot : 0.f;

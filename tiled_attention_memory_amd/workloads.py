@@ -78,13 +78,10 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     NaN is not expected from a normal generator and is not special-cased.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).reshape(-1)
-    out = np.empty(u.shape, dtype=np.uint16)
-    step = 1 << 22  # in pieces, so that large inputs need no GiB-sized temporaries
-    for i in range(0, u.size, step):
-        v = u[i:i + step].astype(np.uint64)
-        out[i:i + step] = ((v + 0x7FFF + ((v >> 16) & 1)) >> 16).astype(np.uint16)
-    return out.reshape(x.shape)
+    u = x.view(np.uint32)
+    # 32-bit sums: a carry out of bit 31 would only reach bit 16 of the shifted
+    # value, which the cast to 16 bits drops, so no wider type is needed
+    return ((u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
 
 
 def draw(shape, seed, mult: float = 1.0) -> np.ndarray:
