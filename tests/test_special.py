@@ -46,9 +46,11 @@ def test_equal_weights_give_running_mean(D, mode):
     assert_lse(to_f64(gpu["lse"]), np.broadcast_to(np.log(np.arange(1, S + 1)), (B, Hq, S)))
 
 
-def test_zero_output_gradient_gives_zero_gradients():
-    say("dO = 0")
-    x = wl.make_inputs(1, 8, 2, 257, 128, seed=(202,))
+@pytest.mark.parametrize("S", [257, 600])
+def test_zero_output_gradient_gives_zero_gradients(S):
+    # S = 600: the fp16 gradient products, with an all-zero dO in every block
+    say(f"dO = 0, S = {S}")
+    x = wl.make_inputs(1, 8, 2, S, 128, seed=(202,))
     x["do"] = np.zeros_like(x["do"])
     gpu = run_gpu(x, True, 1.0 / math.sqrt(128))
     for name in ("dq", "dk", "dv"):
@@ -65,6 +67,46 @@ def test_unusual_scales_against_oracle(scale, k_mult, causal):
     ref = att.backward(q, k, v, do, scale, causal=causal)
     for name in ("o", "dq", "dk", "dv"):
         assert_close(name, to_f64(gpu[name]), ref[name])
+    assert_lse(to_f64(gpu["lse"]), ref["lse"])
+
+
+def _times(bits, factor):
+    """bf16 bit patterns times a power of two (or an array of them): exact in bf16."""
+    return wl.f32_to_bf16_bits((att.bf16_bits_to_f64(bits) * factor).astype(np.float32))
+
+
+@pytest.mark.parametrize("case", ["tiny_dO", "opposite_QK_large_V", "mixed_blocks"])
+def test_fp16_gradient_products_across_magnitudes(case):
+    """Calls over 512 keys or more run the dK/dV products in fp16, with a power-of-two scale per
+    32-row block of Q and dO and per 32 keys of K and V. Far from unit magnitude, and with blocks
+    of very different magnitude, the results must still match the oracle relative to their size
+    (each output is divided by the power of two it scales with before comparing)."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 600, 128
+    causal, scale = True, 1.0 / math.sqrt(D)
+    say(f"fp16 gradient products: {case}")
+    x = wl.make_inputs(B, Hq, Hkv, S, D, seed=(205, len(case)))
+    unit = {"o": 1.0, "dq": 1.0, "dk": 1.0, "dv": 1.0}
+    if case == "tiny_dO":
+        x["do"] = _times(x["do"], 2.0 ** -20)
+        unit.update(dq=2.0 ** -20, dk=2.0 ** -20, dv=2.0 ** -20)
+    elif case == "opposite_QK_large_V":
+        # the scores are unchanged; O and dP scale with V, dQ with V/64, dK with 64 V
+        x["q"] = _times(x["q"], 2.0 ** 6)
+        x["k"] = _times(x["k"], 2.0 ** -6)
+        x["v"] = _times(x["v"], 2.0 ** 9)
+        unit.update(o=2.0 ** 9, dq=2.0 ** 3, dk=2.0 ** 15)
+    else:
+        # 32-row blocks cycle through dO scales 2^-8, 1/2, 1 and Q scales 1/2, 1/8, 1: block
+        # exponents eight binary orders apart, with every output at most of unit size (the
+        # tolerances are absolute)
+        blk = (np.arange(S) // 32) % 3
+        x["do"] = _times(x["do"], np.array([2.0 ** -8, 0.5, 1.0])[blk][None, None, :, None])
+        x["q"] = _times(x["q"], np.array([0.5, 0.125, 1.0])[blk][None, None, :, None])
+    gpu = run_gpu(x, causal, scale)
+    q, k, v, do = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    ref = att.backward(q, k, v, do, scale, causal=causal)
+    for name in ("o", "dq", "dk", "dv"):
+        assert_close(name, to_f64(gpu[name]) / unit[name], ref[name] / unit[name])
     assert_lse(to_f64(gpu["lse"]), ref["lse"])
 
 

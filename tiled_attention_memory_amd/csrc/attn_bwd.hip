@@ -22,7 +22,9 @@
 //             Delta_i - Delta~_i = sum_j dS~_ij =: c_i, so
 //             dQ_i = scale (sum_j dS~_ij K_j - c_i sum_j P_ij K_j), and the exact
 //             Delta_i = Delta~_i + c_i is written back for kernel 3. This removes
-//             the error that rounding O to bf16 puts into Delta.
+//             the error that rounding O to bf16 puts into Delta. For the fp16
+//             dK/dV kernel it also writes fp16 copies of Q and dO and the
+//             block exponents of Q, dO and Delta.
 //   3. dkdv:  key-stationary. One unit = (batch, kv head, 128-key tile, subset
 //             of the group's query heads); 8 waves in pairs own 32 keys per
 //             pair while 64-row Q/dO tiles stream through LDS. In each pair one
@@ -33,9 +35,13 @@
 //             rows; with more than one head subset, fp32 partials go to the
 //             workspace.
 //   4. reduce (only with several subsets): sums the partials in a fixed order.
-// The second operand of every gradient product (P for dV, dS for dK and dQ)
-// enters the bf16 MFMA as a hi + lo pair of bf16 values, so those products
-// carry about 16 significant bits of P and dS instead of 8.
+// Precision of the gradient products (P for dV, dS for dK and dQ): in the dQ
+// kernel, and in the dK/dV kernel of short sequences, dropout and the block
+// protocol, the second operand enters the bf16 MFMA as a hi + lo pair of bf16
+// values, about 16 significant bits. The dK/dV kernel of whole-sequence calls
+// over 512 keys or more instead runs all four of its products in fp16 (11
+// significant bits, one product each) on power-of-two scaled copies of Q and
+// dO that the dQ kernel writes, which removes a third of its matrix work.
 // Every output element is produced by one thread in a fixed order, so the
 // results are bitwise reproducible.
 #include <math.h>
@@ -59,6 +65,7 @@ constexpr int kQBC = 64;    // dq: keys per tile
 constexpr int kKBC = 128;   // dkdv: keys per workgroup
 constexpr int kKBR = 64;    // dkdv: query rows per streamed tile
 constexpr int kTargetUnits = 1024;
+constexpr int kF16MinKeys = 512;
 
 // ---------------------------------------------------------------------------
 // workspace layout
@@ -133,26 +140,36 @@ int choose_head_split(const AttnShape& sh, bool block) {
 }
 
 struct WsLayout {
-  size_t delta, lse2, csum, acc_dq, acc_pk, part, total;
+  size_t delta, lse2, csum, acc_dq, acc_pk, q16, do16, eq, edo, edl, part, total;
   int nsplit;
 };
 
-// Backward workspace. Whole-sequence pass: Delta, lse2 and the dK/dV partials.
-// Block protocol (block = true): also the running c = sum dS~ per row and the
-// fp32 sums of dS~ K and P K over the key blocks seen so far.
+// Backward workspace. Whole-sequence pass: Delta, lse2, the fp16 copies of Q
+// and dO with their block exponents (and that of Delta) for the fp16 dK/dV
+// kernel, and the dK/dV partials. Block protocol (block = true): Delta, lse2,
+// the running c = sum dS~ per row, the fp32 sums of dS~ K and P K over the key
+// blocks seen so far, and the partials.
 WsLayout ws_layout(const AttnShape& sh, bool block = false) {
   WsLayout w;
   const size_t rows = (size_t)sh.B * sh.Hq * sh.Sq;
+  const size_t blocks = (size_t)sh.B * sh.Hq * ((sh.Sq + 31) / 32);
   w.nsplit = choose_head_split(sh, block);
   w.delta = 0;
   w.lse2 = align256(rows * 4);
   size_t off = w.lse2 + align256(rows * 4);
-  w.csum = w.acc_dq = w.acc_pk = 0;
+  w.csum = w.acc_dq = w.acc_pk = w.q16 = w.do16 = w.eq = w.edo = w.edl = 0;
   if (block) {
     w.csum = off;
     w.acc_dq = w.csum + align256(rows * 4);
     w.acc_pk = w.acc_dq + align256(rows * sh.D * 4);
     off = w.acc_pk + align256(rows * sh.D * 4);
+  } else {
+    w.q16 = off;
+    w.do16 = w.q16 + align256(rows * sh.D * 2);
+    w.eq = w.do16 + align256(rows * sh.D * 2);
+    w.edo = w.eq + align256(blocks * 4);
+    w.edl = w.edo + align256(blocks * 4);
+    off = w.edl + align256(blocks * 4);
   }
   w.part = off;
   const size_t kv_elems = (size_t)sh.B * sh.Hkv * sh.Sk * sh.D;
@@ -209,6 +226,11 @@ struct DkdvArgs {
   float scale;
   DropParams drop;  // dropout on the probabilities (DROP kernels only)
   const float2* rope_inv;  // (cos, sin) table [Sk][D/2]: rotate dK back; null = none
+  // fp16 kernels: q and dout are the dQ kernel's fp16 copies, and these its
+  // block exponents of Q, dO and the exact Delta ([B*Hq][ceil(Sq/32)])
+  const int* eq;
+  const int* edo;
+  const int* edl;
   TileSched sched;  // streams = (batch*Hkv + kv head) * nsplit + subset; tiles = key tiles
 };
 
@@ -228,16 +250,30 @@ struct DkdvLayout {
   static constexpr int BYTES = PB + 2 * PB_STAGE;
 };
 
-template <int D, bool CAUSAL, bool DROP = false>
+// F16: every product runs on fp16 operands, one product per gradient with no
+// lo halves. Q and dO come as the dQ kernel's fp16 copies (each 32-row block
+// b scaled by s_Q(b) = 2^(14 - eQ(b)), s_dO(b) = 2^(14 - eD(b))); each wave
+// turns its 32 rows of K or V into fp16 with its own s_K or s_V. The block
+// scales are folded into per-step scalars: S' = s_Q s_K S, so c' = c /
+// (s_Q s_K); the probabilities go to the dV product as P W / s_dO(b), where
+// W = 2^15 min_b s_dO(b) over the unit's blocks keeps them at or below 2^15;
+// and dS goes to the dK product as dS U / s_Q(b), where U is the largest power
+// of two keeping every block's dS at or below 2^15, from the bound
+// |dS| <= |dP| + |Delta| <= D 2^(eD + eV) + 2^eDelta. dV = acc / W and
+// dK = scale acc / U at the end.
+template <int D, bool CAUSAL, bool DROP = false, bool F16 = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(DkdvArgs a) {
   using T = SwzTile<D>;
   using L = DkdvLayout<D>;
+  using Op = std::conditional_t<F16, f16x8, bf16x8>;  // MFMA operand type
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int SLD = T::LOADS / 4;             // streamed Q/dO loads per wave per tile
+  constexpr int kLog2D = D == 128 ? 7 : 6;
   static_assert(kKBR == T::ROWS && kKBC == 2 * T::ROWS, "tile sizes");
   static_assert(L::BYTES <= 160 * 1024, "LDS");
+  static_assert(!(F16 && DROP), "the fp16 kernels run without dropout");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
 
   int stream, t;
@@ -262,14 +298,32 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   const int kvrow = kvb0 + col;        // the key this lane owns
   const uint32_t lds0 = lds_address(smem);
 
-  // K (for S) or V (for dP) rows of this wave's keys as MFMA B operands.
-  bf16x8 kvf[KS];
+  // K (for S) or V (for dP) rows of this wave's keys as MFMA B operands; in
+  // the fp16 kernels scaled by 2^(14 - e_kv) with the exponent of the wave's rows.
+  Op kvf[KS];
+  int e_kv = 0;
   {
     const uint16_t* src = (vrole ? a.k : a.v) + kv_base + (size_t)kvrow * D + 8 * half;
+    bf16x8 raw[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kvf[ks] = kvrow < Sk ? *reinterpret_cast<const bf16x8*>(src + 16 * ks)
+      raw[ks] = kvrow < Sk ? *reinterpret_cast<const bf16x8*>(src + 16 * ks)
                           : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    if constexpr (F16) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t mk = bf16x8_max_mag(raw[ks]);
+        m = m > mk ? m : mk;
+      }
+      e_kv = ceil_log2(__builtin_bit_cast(float, wave_max(m) << 16));
+      const float sc = __builtin_ldexpf(1.f, 14 - e_kv);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kvf[ks] = bf16x8_to_f16x8(raw[ks], sc);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kvf[ks] = raw[ks];
+    }
   }
 
   // Per-lane LDS offsets (see SwzTile) into the stage this wave reads next: rr
@@ -312,6 +366,27 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   const int per_head = max(0, NQ - i_min);  // query tiles visited per head
   const int nsteps = per_head * hps;
 
+  // fp16 kernels: unit-wide exponents over the 32-row blocks the unit visits,
+  // E_dO = max eD (W = 2^(29 - E_dO)) and, for the dS role,
+  // E_U = max (eQ + max(log2 D + eD + eV, eDelta)) (U = 2^(28 - E_U)).
+  const int nblk = (Sq + 31) / 32;
+  int E_dO = kMinExp, E_U = kMinExp;
+  if constexpr (F16) {
+    const int nb = 2 * per_head;  // blocks per head: query tiles i_min .. NQ - 1
+    for (int i = lane; i < nb * hps; i += 64) {
+      const int hh = i / nb;
+      const int blk = 2 * i_min + (i - hh * nb);
+      if (blk < nblk) {
+        const size_t o = ((size_t)b * a.Hq + h_first + hh) * nblk + blk;
+        const int ed = a.edo[o];
+        E_dO = max(E_dO, ed);
+        if (!vrole) E_U = max(E_U, a.eq[o] + max(kLog2D + ed + e_kv, a.edl[o]));
+      }
+    }
+    E_dO = wave_max(E_dO);
+    E_U = wave_max(E_U);
+  }
+
   // Steps visit (query head, query tile) with tiles from the last one down and
   // the subset's heads innermost, so that the units resident at the same time
   // (whatever their key tile) stream the same Q/dO tiles together and share
@@ -335,11 +410,32 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 #pragma unroll
   for (int i = 0; i < SLD; ++i) sld[i] = T::load_src((wave * SLD + i) % T::LOADS, lane);
 
+  // fp16 kernels: the step's block exponents, loaded with its tiles; lanes
+  // 0..3 hold eQ of blocks 0, 1 and eD of blocks 0, 1 of the query tile.
+  int ex4 = 0;
+  struct StepExp {
+    int q[2], d[2];
+  };
+  auto step_exp = [&]() TAM_INLINE {
+    StepExp e;
+    e.q[0] = __builtin_amdgcn_readlane(ex4, 0);
+    e.q[1] = __builtin_amdgcn_readlane(ex4, 1);
+    e.d[0] = __builtin_amdgcn_readlane(ex4, 2);
+    e.d[1] = __builtin_amdgcn_readlane(ex4, 3);
+    return e;
+  };
+
   // Q, dO tiles and their lse2, delta rows of step st (at cursor cu) straight
   // into its stages; rows past Sq read as zeros.
   auto issue = [&](int st, const Cursor& cu) TAM_INLINE {
     const int row0 = cu.it * kKBR;
     const size_t bh = (size_t)b * a.Hq + cu.h;
+    if constexpr (F16) {
+      // every lane loads (a block past the end reads the last one: its rows
+      // are all masked), so no copy of the result has to wait for it
+      const int blk = min(2 * cu.it + (lane & 1), nblk - 1);
+      ex4 = ((lane & 2) ? a.edo : a.eq)[bh * nblk + blk];
+    }
     const int rows_left = Sq - row0;
     const __amdgpu_buffer_rsrc_t rqd = make_rsrc(a.q + (bh * Sq + row0) * D, rows_left * D * 2);
     const __amdgpu_buffer_rsrc_t rdd = make_rsrc(a.dout + (bh * Sq + row0) * D, rows_left * D * 2);
@@ -383,11 +479,11 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs)
-          x[qs] = mfma32(*reinterpret_cast<const bf16x8*>(smem + rr[ks] + qs * 32 * T::ROW_BYTES), kvf[ks], x[qs]);
+          x[qs] = mfma32(*reinterpret_cast<const Op*>(smem + rr[ks] + qs * 32 * T::ROW_BYTES), kvf[ks], x[qs]);
     } else if (runs(MASKED, it, 1)) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        x[1] = mfma32(*reinterpret_cast<const bf16x8*>(smem + rr[ks] + 32 * T::ROW_BYTES), kvf[ks], x[1]);
+        x[1] = mfma32(*reinterpret_cast<const Op*>(smem + rr[ks] + 32 * T::ROW_BYTES), kvf[ks], x[1]);
     }
   };
   auto rows_by_keys_at = [&](bool masked, int it, f32x16 (&x)[2]) TAM_INLINE {
@@ -404,7 +500,8 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   // copy of it per loop body: every accumulator value then feeds exactly one
   // matrix instruction, so the compiler accumulates in place instead of
   // keeping a second copy of dV^T/dK^T.
-  auto accumulate = [&](const bf16x8 (&hi)[2][2], const bf16x8 (&lo)[2][2]) TAM_INLINE {
+  // (fp16 kernels: one product on G alone; the lo array is unused.)
+  auto accumulate = [&](const Op (&hi)[2][2], const Op (&lo)[2][2]) TAM_INLINE {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
@@ -412,24 +509,29 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int ro = (qs * 32 + k2 * 16) * T::ROW_BYTES;
-          const bf16x8 at = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(smem + ro + tt[db][0]),
-                                             reinterpret_cast<const uint16_t*>(smem + ro + tt[db][1]));
+          const Op at = __builtin_bit_cast(Op, lds_read_tr_pair(reinterpret_cast<const uint16_t*>(smem + ro + tt[db][0]),
+                                                                reinterpret_cast<const uint16_t*>(smem + ro + tt[db][1])));
           acc[db] = mfma32(at, hi[qs][k2], acc[db]);
-          acc[db] = mfma32(at, lo[qs][k2], acc[db]);
+          if constexpr (!F16) acc[db] = mfma32(at, lo[qs][k2], acc[db]);
         }
   };
 
   // P role, one step: P = exp2(S c - lse2) with the tile's mask, to the
   // partner (with dropout: the sign carries the keep bit) and as hi + lo
   // pairs for dV (with dropout: the kept probabilities scaled by r).
+  // (fp16 kernels: with the step's scales, P W / s_dO as one fp16 operand;
+  // the partner gets the same scaled values.)
   auto probabilities = [&](auto masked_tag, int st, int it, uint32_t bhq, bool masked, const f32x16 (&x)[2],
-                           bf16x8 (&hi)[2][2], bf16x8 (&lo)[2][2]) TAM_INLINE {
+                           const StepExp& ex, Op (&hi)[2][2], Op (&lo)[2][2]) TAM_INLINE {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const float* Fs = reinterpret_cast<const float*>(smem + f_at(st));
     float* pb = pb_at(st);
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const bool run = runs(masked, it, qs);
+      // c' = c / (s_Q s_K) and log2(W / s_dO) of this 32-row block
+      const float cq = F16 ? __builtin_ldexpf(c, ex.q[qs] + e_kv - 28) : c;
+      const float lsh = F16 ? (float)(15 - E_dO + ex.d[qs]) : 0.f;
       float p[16];
       // Dropout bytes: the four lanes of a quad hold keys 4m .. 4m + 3 and need
       // the same four generator calls (row groups i = 0..3); lane 4m + j makes
@@ -447,7 +549,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * i + r;
-          float e = fast_exp2(fmaf(x[qs][v], c, -l2[r]));
+          float e = fast_exp2(fmaf(x[qs][v], cq, F16 ? lsh - l2[r] : -l2[r]));
           if (MASKED) {
             const int qrow = it * kKBR + qs * 32 + 8 * i + 4 * half + r;
             // bitwise &: every term is evaluated, so the select stays branch-free
@@ -460,22 +562,40 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
             p[v] = keep ? e * a.drop.r : 0.f;
           } else {
             p[v] = e;
-            pb[(16 * qs + v) * 64] = e;
+            if constexpr (!F16) pb[(16 * qs + v) * 64] = e;
           }
         }
       }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) split_bf16x8(p + 8 * k2, &hi[qs][k2], &lo[qs][k2]);
+      for (int k2 = 0; k2 < 2; ++k2) {
+        if constexpr (F16) {
+          // the partner takes the same fp16 pairs: dword w of (qs, k2) holds
+          // elements 8 k2 + 2w and 8 k2 + 2w + 1
+          hi[qs][k2] = pack_f16x8(p + 8 * k2);
+          const u32x4 w4 = __builtin_bit_cast(u32x4, hi[qs][k2]);
+          uint32_t* pw = reinterpret_cast<uint32_t*>(pb);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pw[(8 * qs + 4 * k2 + w) * 64] = w4[w];
+        } else {
+          split_bf16x8(p + 8 * k2, &hi[qs][k2], &lo[qs][k2]);
+        }
+      }
     }
   };
 
   // dS role, second half of step st: dS = P (dP - Delta) from the partner's P
-  // and the dP held in x since the step before, as hi + lo pairs.
-  auto grad_scores = [&](int st, const f32x16 (&x)[2], bf16x8 (&hi)[2][2], bf16x8 (&lo)[2][2]) TAM_INLINE {
+  // and the dP held in x since the step before, as hi + lo pairs. (fp16
+  // kernels: P arrives as P W / s_dO and x holds s_dO s_V dP, so
+  // P W/s_dO (x k - Delta m) with k = U / (W s_V s_Q) and m = s_dO s_V k is
+  // dS U / s_Q, one fp16 operand.)
+  auto grad_scores = [&](int st, const f32x16 (&x)[2], const StepExp& ex, Op (&hi)[2][2],
+                         Op (&lo)[2][2]) TAM_INLINE {
     const float* Fs = reinterpret_cast<const float*>(smem + f_at(st));
     const float* pb = pb_at(st);
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
+      const float kap = F16 ? __builtin_ldexpf(1.f, -29 - E_U + E_dO + e_kv + ex.q[qs]) : 1.f;
+      const float mu = F16 ? __builtin_ldexpf(1.f, -1 - ex.d[qs] - E_U + E_dO + ex.q[qs]) : 1.f;
       float ds[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -483,13 +603,25 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * i + r;
-          const float pv = pb[(16 * qs + v) * 64];
-          ds[v] = DROP ? fabsf(pv) * ((__builtin_signbit(pv) ? 0.f : a.drop.r) * x[qs][v] - dl4[r])
-                       : pv * (x[qs][v] - dl4[r]);
+          if constexpr (F16) {
+            // P as the partner's fp16 pair; the widening folds into the multiply
+            const uint32_t w = reinterpret_cast<const uint32_t*>(pb)[(8 * qs + 4 * (v >> 3) + ((v & 7) >> 1)) * 64];
+            const float pv = (float)__builtin_bit_cast(f16x2, w)[v & 1];
+            ds[v] = fmaf(pv, fmaf(x[qs][v], kap, -dl4[r] * mu), 0.f);
+          } else {
+            const float pv = pb[(16 * qs + v) * 64];
+            ds[v] = DROP ? fabsf(pv) * ((__builtin_signbit(pv) ? 0.f : a.drop.r) * x[qs][v] - dl4[r])
+                         : pv * (x[qs][v] - dl4[r]);
+          }
         }
       }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) split_bf16x8(ds + 8 * k2, &hi[qs][k2], &lo[qs][k2]);
+      for (int k2 = 0; k2 < 2; ++k2) {
+        if constexpr (F16)
+          hi[qs][k2] = pack_f16x8(ds + 8 * k2);
+        else
+          split_bf16x8(ds + 8 * k2, &hi[qs][k2], &lo[qs][k2]);
+      }
     }
   };
 
@@ -512,14 +644,16 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
         const int it = cur.it;
         const bool masked = masked_at(it);
         const uint32_t bhq = (uint32_t)(b * a.Hq + cur.h);
+        StepExp ex{};
+        if constexpr (F16) ex = step_exp();  // loaded with this step's tiles, before the barrier
         f32x16 x[2];
         rows_by_keys_at(masked, it, x);
         if (st + 1 < nsteps) issue(st + 1, nxt);  // after the score products: the issue stalls overlap them
-        bf16x8 hi[2][2], lo[2][2];
+        Op hi[2][2], lo[2][2];
         if (masked)
-          probabilities(std::true_type{}, st, it, bhq, masked, x, hi, lo);
+          probabilities(std::true_type{}, st, it, bhq, masked, x, ex, hi, lo);
         else
-          probabilities(std::false_type{}, st, it, bhq, masked, x, hi, lo);
+          probabilities(std::false_type{}, st, it, bhq, masked, x, ex, hi, lo);
         accumulate(hi, lo);
         move_rr(q_next(st));
         move_tt(do_next(st));
@@ -531,6 +665,8 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
       __syncthreads();  // the partner's last phase
     } else {
       f32x16 x[2];  // dP of the step before, carried over the barrier
+      StepExp ex_prev{};  // that step's exponents (fp16 kernels)
+      if constexpr (F16) ex_prev = step_exp();
       if (nsteps > 1) issue(1, nxt);
       rows_by_keys_at(masked_at(cur.it), cur.it, x);
       move_rr(do_next(0));
@@ -539,20 +675,23 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
       wait_loads();
       __syncthreads();
       for (int st = 1; st < nsteps; ++st) {
+        StepExp ex_cur{};
+        if constexpr (F16) ex_cur = step_exp();
         if (st + 1 < nsteps) issue(st + 1, nxt);
-        bf16x8 hi[2][2], lo[2][2];
-        grad_scores(st - 1, x, hi, lo);
+        Op hi[2][2], lo[2][2];
+        grad_scores(st - 1, x, ex_prev, hi, lo);
         accumulate(hi, lo);
         move_tt(q_next(st - 1));
         rows_by_keys_at(masked_at(cur.it), cur.it, x);
         move_rr(do_next(st));
         advance(cur);
         advance(nxt);
+        ex_prev = ex_cur;
         wait_loads();
         __syncthreads();
       }
-      bf16x8 hi[2][2], lo[2][2];
-      grad_scores(nsteps - 1, x, hi, lo);
+      Op hi[2][2], lo[2][2];
+      grad_scores(nsteps - 1, x, ex_prev, hi, lo);
       accumulate(hi, lo);
       __syncthreads();
     }
@@ -560,7 +699,9 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 
   // lane holds key kvrow, head-dim entries 32db + 8i + 4half + (0..3)
   if (kvrow < Sk) {
-    const float mul = vrole ? 1.f : a.scale;
+    // fp16 kernels: dV = acc / W, dK = scale acc / U
+    const float mul = F16 ? (vrole ? __builtin_ldexpf(1.f, E_dO - 29) : a.scale * __builtin_ldexpf(1.f, E_U - 28))
+                          : (vrole ? 1.f : a.scale);
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] *= mul;
     if (!vrole && a.rope_inv) {
@@ -646,6 +787,14 @@ struct DqArgs {
   float* acc_dq;
   float* acc_pk;
   float* acc_c;
+  // When set (whole-sequence calls without dropout): fp16 copies of Q and dO
+  // for the dK/dV kernel, each 32-row block scaled by 2^(14 - e), and the
+  // block exponents e of Q, dO and the exact Delta, [B*Hq][ceil(Sq/32)] each.
+  uint16_t* q16;
+  uint16_t* do16;
+  int* eq;
+  int* edo;
+  int* edl;
   int Hq, Hkv, Sq, Sk, dlt;
   float c;
   float scale;
@@ -736,6 +885,30 @@ void attn_bwd_dq_kernel(DqArgs a) {
     }
   }
   if (a.o && !prole) rowval = sum_halves(rowval);  // every lane takes part in the exchange
+
+  // fp16 copy of this pair's 32 rows of Q (P role) or dO (dS role) with the
+  // rows' block exponent, for the dK/dV kernel. (Stored here, before the
+  // tiles: stores count among the loads every barrier waits for, and spread
+  // over the tile loop they cost registers.)
+  const int nblk = (Sq + 31) / 32;
+  const size_t eidx = (size_t)bh * nblk + (wrow0 >> 5);
+  if (a.q16) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t mk = bf16x8_max_mag(xf[ks]);
+      m = m > mk ? m : mk;
+    }
+    const int e = ceil_log2(__builtin_bit_cast(float, wave_max(m) << 16));
+    const float sc = __builtin_ldexpf(1.f, 14 - e);
+    if (qrow < Sq) {
+      uint16_t* dst = (prole ? a.q16 : a.do16) + q_base + (size_t)qrow * D + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<f16x8*>(dst + 16 * ks) = bf16x8_to_f16x8(xf[ks], sc);
+    }
+    if (lane == 0 && wrow0 < Sq) (prole ? a.eq : a.edo)[eidx] = e;
+  }
+
 
   // Per-lane LDS offsets (see SwzTile) into the stage this wave reads next:
   // roff for the key-by-row products (K for the P role, V for the dS role),
@@ -991,6 +1164,10 @@ void attn_bwd_dq_kernel(DqArgs a) {
   __syncthreads();
   if (prole) return;
   const float corr = sum_halves(csum);  // Delta_i - Delta~_i
+  if (a.edl) {
+    const float dm = wave_max(qrow < Sq ? fabsf(rowval + corr) : 0.f);
+    if (lane == 0 && wrow0 < Sq) a.edl[eidx] = ceil_log2(dm);
+  }
   if (qrow < Sq) {
     // dQ = scale (sum dS~ K - c P K); element v of block db is column
     // 32db + 8(v/4) + 4half + v%4
@@ -1067,6 +1244,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_end_kernel(const float* 
 // ---------------------------------------------------------------------------
 struct Ws {
   float *delta, *lse2, *csum, *acc_dq, *acc_pk, *part;
+  uint16_t *q16, *do16;
+  int *eq, *edo, *edl;
   WsLayout w;
   Ws(const AttnShape& sh, void* base, bool block) : w(ws_layout(sh, block)) {
     char* b = static_cast<char*>(base);
@@ -1075,8 +1254,18 @@ struct Ws {
     csum = block ? reinterpret_cast<float*>(b + w.csum) : nullptr;
     acc_dq = block ? reinterpret_cast<float*>(b + w.acc_dq) : nullptr;
     acc_pk = block ? reinterpret_cast<float*>(b + w.acc_pk) : nullptr;
+    q16 = block ? nullptr : reinterpret_cast<uint16_t*>(b + w.q16);
+    do16 = block ? nullptr : reinterpret_cast<uint16_t*>(b + w.do16);
+    eq = block ? nullptr : reinterpret_cast<int*>(b + w.eq);
+    edo = block ? nullptr : reinterpret_cast<int*>(b + w.edo);
+    edl = block ? nullptr : reinterpret_cast<int*>(b + w.edl);
     part = reinterpret_cast<float*>(b + w.part);
   }
+  // The fp16 dK/dV kernel runs on whole-sequence calls without dropout over
+  // at least kF16MinKeys keys: below that its saving (which grows with the
+  // keys each row sees) does not repay the fp16 copies the dQ kernel writes
+  // (which grow with the rows alone).
+  bool f16(const AttnShape& sh) const { return q16 != nullptr && sh.drop_t == 0 && sh.Sk >= kF16MinKeys; }
 };
 
 template <int D>
@@ -1121,6 +1310,12 @@ hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, 
   a.acc_dq = dq ? nullptr : ws.acc_dq;
   a.acc_pk = dq ? nullptr : ws.acc_pk;
   a.acc_c = dq ? nullptr : ws.csum;
+  const bool f16 = dq && ws.f16(sh);
+  a.q16 = f16 ? ws.q16 : nullptr;
+  a.do16 = f16 ? ws.do16 : nullptr;
+  a.eq = f16 ? ws.eq : nullptr;
+  a.edo = f16 ? ws.edo : nullptr;
+  a.edl = f16 ? ws.edl : nullptr;
   a.Hq = sh.Hq;
   a.Hkv = sh.Hkv;
   a.Sq = sh.Sq;
@@ -1143,10 +1338,14 @@ template <int D, bool CAUSAL>
 hipError_t launch_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const uint16_t* dout, uint16_t* dk, uint16_t* dv, const Ws& ws, hipStream_t stream) {
   DkdvArgs a;
-  a.q = q;
+  const bool f16 = ws.f16(sh);
+  a.q = f16 ? ws.q16 : q;
   a.k = k;
   a.v = v;
-  a.dout = dout;
+  a.dout = f16 ? ws.do16 : dout;
+  a.eq = f16 ? ws.eq : nullptr;
+  a.edo = f16 ? ws.edo : nullptr;
+  a.edl = f16 ? ws.edl : nullptr;
   a.delta = ws.delta;
   a.lse2 = ws.lse2;
   a.dk = dk;
@@ -1167,6 +1366,7 @@ hipError_t launch_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k
   a.sched.chunk = (a.sched.BH + 7) / 8;
   void* args[] = {&a};
   const void* kern = a.drop.t ? reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, true>)
+                     : f16    ? reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, false, true>)
                               : reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, false>);
   return hipLaunchKernel(kern, dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
 }

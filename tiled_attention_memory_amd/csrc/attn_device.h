@@ -16,6 +16,8 @@ namespace tam {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -32,6 +34,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// The same product on fp16 operands (v_mfma_f32_32x32x16_f16, same layouts).
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Two 16-bit transposed LDS reads (rows r0..r0+3 and r0+8..r0+11 of the
@@ -125,6 +131,78 @@ __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8* hi, bf16x8*
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+
+// Round two floats to fp16 (nearest even) and pack them, first in the low half.
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  f16x2 h = __builtin_convertvector(v, f16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ f16x8 pack_f16x8(const float* x) {
+  u32x4 u = {pack_f16(x[0], x[1]), pack_f16(x[2], x[3]), pack_f16(x[4], x[5]), pack_f16(x[6], x[7])};
+  return __builtin_bit_cast(f16x8, u);
+}
+
+// Power-of-two scaling into fp16 operands. A block of values whose largest
+// magnitude is m gets the exponent e = ceil(log2 m), clamped to
+// [kMinExp, kMaxExp] (an all-zero block gets kMinExp), and is held as
+// x * 2^(14 - e): every magnitude is then at most 2^14 (fp16 reaches 65504),
+// and a bf16 value converts exactly unless it lies more than 2^28 below m.
+constexpr int kMinExp = -60, kMaxExp = 128;
+__device__ __forceinline__ int ceil_log2(float m) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, m) & 0x7fffffffu;
+  const int E = (int)(u >> 23);
+  if (E == 0) return kMinExp;  // zero, or below the fp32 normal range
+  const int e = E - 127 + ((u & 0x7fffffu) != 0);
+  return e < kMinExp ? kMinExp : e > kMaxExp ? kMaxExp : e;
+}
+
+// Largest magnitude among eight bf16 values, as a bf16 bit pattern (sign clear):
+// for finite values the patterns order like the magnitudes.
+__device__ __forceinline__ uint32_t bf16x8_max_mag(const bf16x8& x) {
+  const u32x4 u = __builtin_bit_cast(u32x4, x);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = u[i] & 0x7fffu, hi = (u[i] >> 16) & 0x7fffu;
+    m = m > lo ? m : lo;
+    m = m > hi ? m : hi;
+  }
+  return m;
+}
+
+// Eight bf16 values times s (a power of two) as fp16, rounded to nearest even.
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(const bf16x8& x, float s) {
+  const u32x4 u = __builtin_bit_cast(u32x4, x);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_f16(bf16_lo(u[i]) * s, bf16_hi(u[i]) * s);
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// Largest value over the 64 lanes of the wave (every lane gets it).
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t y = __shfl_xor(x, off);
+    x = x > y ? x : y;
+  }
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const int y = __shfl_xor(x, off);
+    x = x > y ? x : y;
+  }
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
 
 // ---------------------------------------------------------------------------
 // 64-row LDS tiles of bf16 rows, filled straight from global memory
