@@ -117,12 +117,14 @@ def test_workspace_query():
     lib = tam.load()
     assert lib.attn_bwd_workspace_bytes(1, 4, 2, 128, 128, None) == 1
     # grows with the sequence: per query row two floats, an fp16 copy of its Q and dO rows and
-    # (every 32 rows) three exponents, plus dK/dV partials when the heads are split
+    # (every 32 rows) three exponents; per key an fp16 copy of its K row and (every 64 keys) two
+    # exponents; plus dK/dV partials when the heads are split
     B, Hq, Hkv, S, D = 1, 8, 1, 81920, 128
     rows = B * Hq * S
-    per_rows = rows * (2 * 4 + 2 * D * 2) + 3 * 4 * B * Hq * ((S + 31) // 32)
+    per_rows = (rows * (2 * 4 + 2 * D * 2) + 3 * 4 * B * Hq * ((S + 31) // 32)
+                + B * Hkv * S * D * 2 + 2 * 4 * B * Hkv * ((S + 63) // 64))
     n = ws_bytes(Hq=Hq, Hkv=Hkv, S=S)
-    assert per_rows <= n <= per_rows + 8 * 2 * B * Hkv * S * D * 4 + 8 * 256
+    assert per_rows <= n <= per_rows + 8 * 2 * B * Hkv * S * D * 4 + 12 * 256
 
 
 @pytest.mark.parametrize("name", ["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"])

@@ -31,13 +31,14 @@ def test_scheduler(tmp_path):
 def _head_split(B, Hq, Hkv, S, D):
     """Head subsets the dK/dV kernel uses for a whole-sequence call, read off the workspace size
     (two fp32 rows of B*Hq*S, two fp16 copies of [B*Hq*S, D], three int rows of B*Hq*ceil(S/32)
-    block exponents, each padded to 256 bytes, then nsplit x 2 partial copies of dK/dV when
-    nsplit > 1)."""
+    block exponents, an fp16 copy of K and two int rows of B*Hkv*ceil(S/64) tile exponents, each
+    padded to 256 bytes, then nsplit x 2 partial copies of dK/dV when nsplit > 1)."""
     import tiled_attention_memory_amd as tam
     ws = tam.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)
     pad = lambda n: (n + 255) // 256 * 256
     base = (2 * pad(B * Hq * S * 4) + 2 * pad(B * Hq * S * D * 2)
-            + 3 * pad(B * Hq * ((S + 31) // 32) * 4))
+            + 3 * pad(B * Hq * ((S + 31) // 32) * 4)
+            + pad(B * Hkv * S * D * 2) + 2 * pad(B * Hkv * ((S + 63) // 64) * 4))
     if ws == base:
         return 1
     part = 2 * B * Hkv * S * D * 4

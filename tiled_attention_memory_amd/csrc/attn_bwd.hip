@@ -35,13 +35,14 @@
 //             rows; with more than one head subset, fp32 partials go to the
 //             workspace.
 //   4. reduce (only with several subsets): sums the partials in a fixed order.
-// Precision of the gradient products (P for dV, dS for dK and dQ): in the dQ
-// kernel, and in the dK/dV kernel of short sequences, dropout and the block
-// protocol, the second operand enters the bf16 MFMA as a hi + lo pair of bf16
-// values, about 16 significant bits. The dK/dV kernel of whole-sequence calls
-// over 512 keys or more instead runs all four of its products in fp16 (11
-// significant bits, one product each) on power-of-two scaled copies of Q and
-// dO that the dQ kernel writes, which removes a third of its matrix work.
+// Precision of the gradient products (P for dV, dS for dK and dQ): for short
+// sequences, dropout and the block protocol, the second operand enters the
+// bf16 MFMA as a hi + lo pair of bf16 values, about 16 significant bits.
+// Whole-sequence calls without dropout over 512 keys or more instead run every
+// product of the dK/dV kernel, and those with K in the dQ kernel (S, P K and
+// dQ), in fp16 (11 significant bits, one product each) on power-of-two scaled
+// operands: copies of Q and dO that the dQ kernel writes, and a copy of K made
+// by a small kernel of its own (1b) before it.
 // Every output element is produced by one thread in a fixed order, so the
 // results are bitwise reproducible.
 #include <math.h>
@@ -140,13 +141,14 @@ int choose_head_split(const AttnShape& sh, bool block) {
 }
 
 struct WsLayout {
-  size_t delta, lse2, csum, acc_dq, acc_pk, q16, do16, eq, edo, edl, part, total;
+  size_t delta, lse2, csum, acc_dq, acc_pk, q16, do16, eq, edo, edl, k16, ek, ev, part, total;
   int nsplit;
 };
 
 // Backward workspace. Whole-sequence pass: Delta, lse2, the fp16 copies of Q
 // and dO with their block exponents (and that of Delta) for the fp16 dK/dV
-// kernel, and the dK/dV partials. Block protocol (block = true): Delta, lse2,
+// kernel, the fp16 copy of K with its tile exponents (and those of V) for the
+// fp16 dQ kernel, and the dK/dV partials. Block protocol (block = true): Delta, lse2,
 // the running c = sum dS~ per row, the fp32 sums of dS~ K and P K over the key
 // blocks seen so far, and the partials.
 WsLayout ws_layout(const AttnShape& sh, bool block = false) {
@@ -157,7 +159,7 @@ WsLayout ws_layout(const AttnShape& sh, bool block = false) {
   w.delta = 0;
   w.lse2 = align256(rows * 4);
   size_t off = w.lse2 + align256(rows * 4);
-  w.csum = w.acc_dq = w.acc_pk = w.q16 = w.do16 = w.eq = w.edo = w.edl = 0;
+  w.csum = w.acc_dq = w.acc_pk = w.q16 = w.do16 = w.eq = w.edo = w.edl = w.k16 = w.ek = w.ev = 0;
   if (block) {
     w.csum = off;
     w.acc_dq = w.csum + align256(rows * 4);
@@ -169,7 +171,11 @@ WsLayout ws_layout(const AttnShape& sh, bool block = false) {
     w.eq = w.do16 + align256(rows * sh.D * 2);
     w.edo = w.eq + align256(blocks * 4);
     w.edl = w.edo + align256(blocks * 4);
-    off = w.edl + align256(blocks * 4);
+    const size_t kv_tiles = (size_t)sh.B * sh.Hkv * ((sh.Sk + 63) / 64);
+    w.k16 = w.edl + align256(blocks * 4);
+    w.ek = w.k16 + align256((size_t)sh.B * sh.Hkv * sh.Sk * sh.D * 2);
+    w.ev = w.ek + align256(kv_tiles * 4);
+    off = w.ev + align256(kv_tiles * 4);
   }
   w.part = off;
   const size_t kv_elems = (size_t)sh.B * sh.Hkv * sh.Sk * sh.D;
@@ -205,6 +211,60 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(const uint16_t*
     // a row that sees no key at all has LSE = -inf; +inf here makes every
     // recomputed probability of that row exactly 0
     lse2[row] = lse[row] == -INFINITY ? INFINITY : lse[row] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1b. fp16 copy of K with one exponent per 64-key tile, and the exponent of
+//     each V tile (for the fp16 dQ kernel): tile t of a kv head is stored as
+//     K * 2^(14 - ek(t)), ek = ceil(log2 of the tile's largest |K|)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_k16_kernel(const uint16_t* k, const uint16_t* v,
+                                                                uint16_t* k16, int* ek, int* ev, int Sk,
+                                                                int ntile) {
+  constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  constexpr int NC = 64 * CPR / kThreads;      // chunks per thread
+  __shared__ uint32_t red[2][kThreads / 64];
+  const int tile = blockIdx.x % ntile;
+  const size_t head = blockIdx.x / ntile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t base = (head * Sk + (size_t)tile * 64) * D;
+  bf16x8 kc[NC];
+  uint32_t mk = 0, mv = 0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = tid + kThreads * i, row = c / CPR;
+    const bool ok = tile * 64 + row < Sk;
+    const size_t off = base + (size_t)c * 8;   // chunks of consecutive rows are contiguous
+    kc[i] = ok ? *reinterpret_cast<const bf16x8*>(k + off) : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    const bf16x8 vc = ok ? *reinterpret_cast<const bf16x8*>(v + off) : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    const uint32_t a = bf16x8_max_mag(kc[i]), b = bf16x8_max_mag(vc);
+    mk = mk > a ? mk : a;
+    mv = mv > b ? mv : b;
+  }
+  mk = wave_max(mk);
+  mv = wave_max(mv);
+  if (lane == 0) {
+    red[0][wave] = mk;
+    red[1][wave] = mv;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    mk = mk > red[0][w] ? mk : red[0][w];
+    mv = mv > red[1][w] ? mv : red[1][w];
+  }
+  const int e = ceil_log2(__builtin_bit_cast(float, mk << 16));
+  const float sc = __builtin_ldexpf(1.f, 14 - e);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = tid + kThreads * i, row = c / CPR;
+    if (tile * 64 + row < Sk) *reinterpret_cast<f16x8*>(k16 + base + (size_t)c * 8) = bf16x8_to_f16x8(kc[i], sc);
+  }
+  if (tid == 0) {
+    ek[head * ntile + tile] = e;
+    ev[head * ntile + tile] = ceil_log2(__builtin_bit_cast(float, mv << 16));
   }
 }
 
@@ -316,7 +376,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
         const uint32_t mk = bf16x8_max_mag(raw[ks]);
         m = m > mk ? m : mk;
       }
-      e_kv = ceil_log2(__builtin_bit_cast(float, wave_max(m) << 16));
+      e_kv = __builtin_amdgcn_readfirstlane(ceil_log2(__builtin_bit_cast(float, wave_max(m) << 16)));
       const float sc = __builtin_ldexpf(1.f, 14 - e_kv);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kvf[ks] = bf16x8_to_f16x8(raw[ks], sc);
@@ -383,8 +443,8 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
         if (!vrole) E_U = max(E_U, a.eq[o] + max(kLog2D + ed + e_kv, a.edl[o]));
       }
     }
-    E_dO = wave_max(E_dO);
-    E_U = wave_max(E_U);
+    E_dO = __builtin_amdgcn_readfirstlane(wave_max(E_dO));
+    E_U = __builtin_amdgcn_readfirstlane(wave_max(E_U));
   }
 
   // Steps visit (query head, query tile) with tiles from the last one down and
@@ -795,6 +855,10 @@ struct DqArgs {
   int* eq;
   int* edo;
   int* edl;
+  // fp16 kernels: k is the fp16 copy of K, and these its tile exponents and
+  // those of V ([B*Hkv][ceil(Sk/64)])
+  const int* ek;
+  const int* ev;
   int Hq, Hkv, Sq, Sk, dlt;
   float c;
   float scale;
@@ -814,17 +878,30 @@ struct DqLayout {
   static constexpr int PB = 5 * T::BYTES;
   static constexpr int PB_BLOCK = 32 * kQBC * 4;  // 32 rows x 64 keys fp32
   static constexpr int PB_STAGE = 4 * PB_BLOCK;
-  static constexpr int BYTES = PB + 2 * PB_STAGE;
+  static constexpr int EK = PB + 2 * PB_STAGE;    // fp16 kernels: K tile exponent per K stage (one wave load each)
+  static constexpr int BYTES = EK + 3 * 256;
   static_assert(4 * (D / 32) * 16 * 64 * 4 <= PB, "final hand-off fits in the stages");
 };
 
-template <int D, bool CAUSAL, bool DROP = false>
+// F16: the products with K (S, P K and dQ) run on fp16 operands, one product
+// each: K comes as the fp16 copy (tile t scaled by s_K(t) = 2^(14 - ek(t))),
+// the P role turns its Q rows into fp16 with their block scale s_Q, so
+// S' = s_K s_Q S and c' = c / (s_K s_Q) per tile; P goes to the P K product and
+// to the partner as P W / s_K(t), W = 2^(29 - E_K) with E_K = max ek over the
+// unit's tiles; the dS role forms dS U / s_K(t) from it with one unit-wide
+// factor, U the largest power of two keeping every dS at or below 2^15 by
+// |dS~| <= |dP| + |Delta~| <= 2 D 2^(eD + E_V) (E_V = max ev, since O is a
+// mean of V rows). dP = V dO^T stays in bf16. dQ = scale (acc / U - c PK / W).
+template <int D, bool CAUSAL, bool DROP = false, bool F16 = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(DqArgs a) {
   using T = SwzTile<D>;
   using L = DqLayout<D>;
+  using KOp = std::conditional_t<F16, f16x8, bf16x8>;  // operand type of the products with K
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int kLog2D = D == 128 ? 7 : 6;
+  static_assert(!(F16 && DROP), "the fp16 kernels run without dropout");
   constexpr int NLD = T::LOADS / 4;   // K and V loads per wave per tile
   static_assert(kQBC == T::ROWS && kQBR == 128, "tile sizes");
   static_assert(L::BYTES <= 160 * 1024, "LDS");
@@ -890,23 +967,33 @@ void attn_bwd_dq_kernel(DqArgs a) {
   // rows' block exponent, for the dK/dV kernel. (Stored here, before the
   // tiles: stores count among the loads every barrier waits for, and spread
   // over the tile loop they cost registers.)
+  // (fp16 kernels: the P role keeps these fp16 values of Q as its operands,
+  // and both roles use the block exponent e_blk.)
   const int nblk = (Sq + 31) / 32;
   const size_t eidx = (size_t)bh * nblk + (wrow0 >> 5);
-  if (a.q16) {
+  int e_blk = 0;
+  if (F16 || a.q16) {
     uint32_t m = 0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint32_t mk = bf16x8_max_mag(xf[ks]);
       m = m > mk ? m : mk;
     }
-    const int e = ceil_log2(__builtin_bit_cast(float, wave_max(m) << 16));
-    const float sc = __builtin_ldexpf(1.f, 14 - e);
-    if (qrow < Sq) {
+    e_blk = __builtin_amdgcn_readfirstlane(ceil_log2(__builtin_bit_cast(float, wave_max(m) << 16)));
+    const float sc = __builtin_ldexpf(1.f, 14 - e_blk);
+    f16x8 h[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) h[ks] = bf16x8_to_f16x8(xf[ks], sc);
+    if (a.q16 && qrow < Sq) {
       uint16_t* dst = (prole ? a.q16 : a.do16) + q_base + (size_t)qrow * D + 8 * half;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<f16x8*>(dst + 16 * ks) = bf16x8_to_f16x8(xf[ks], sc);
+      for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<f16x8*>(dst + 16 * ks) = h[ks];
     }
-    if (lane == 0 && wrow0 < Sq) (prole ? a.eq : a.edo)[eidx] = e;
+    if (a.q16 && lane == 0 && wrow0 < Sq) (prole ? a.eq : a.edo)[eidx] = e_blk;
+    if (F16 && prole) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) xf[ks] = __builtin_bit_cast(bf16x8, h[ks]);
+    }
   }
 
 
@@ -916,7 +1003,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
   // a uniform step, so that a runtime stage costs no registers.
   const int i16 = lane & 15;
   const int dsub = 16 * ((lane >> 4) & 1);
-  int roff[KS], toff[DB][2], loff[NLD];
+  int roff[KS], toff[DB][2];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) roff[ks] = (prole ? L::K0 : L::V0) + T::chunk_off(col, 2 * ks + half);
 #pragma unroll
@@ -924,8 +1011,6 @@ void attn_bwd_dq_kernel(DqArgs a) {
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi)
       toff[db][hi] = L::K0 + T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) loff[i] = T::load_src((wave * NLD + i) % T::LOADS, lane);
   // stage step after tile j: K stages cycle through three, V stages through two
   auto k_next = [&](int j) TAM_INLINE { return j % 3 == 2 ? -2 * T::BYTES : T::BYTES; };
   auto v_next = [&](int j) TAM_INLINE { return (j & 1) ? -T::BYTES : T::BYTES; };
@@ -949,17 +1034,40 @@ void attn_bwd_dq_kernel(DqArgs a) {
   // the last key any row of the unit may see is last_row + dlt
   const int ntiles = CAUSAL ? (last_row + dlt < 0 ? 0 : min(n_kv, (last_row + dlt) / kQBC + 1)) : n_kv;
 
+  // fp16 kernels: E_K and E_V over the unit's key tiles; the exponent of each
+  // tile travels with it into LDS (beside its K stage), so that it waits with
+  // the tile's own loads and holds no register across the loop
+  const size_t tbase = ((size_t)b * a.Hkv + kvh) * n_kv;
+  int E_K = kMinExp, E_V = kMinExp;
+  if constexpr (F16) {
+    for (int t = lane; t < ntiles; t += 64) {
+      E_K = max(E_K, a.ek[tbase + t]);
+      E_V = max(E_V, a.ev[tbase + t]);
+    }
+    E_K = __builtin_amdgcn_readfirstlane(wave_max(E_K));
+    E_V = __builtin_amdgcn_readfirstlane(wave_max(E_V));
+  }
+  auto tile_exp = [&](int j) TAM_INLINE {
+    return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(smem + L::EK + (j % 3) * 256));
+  };
+
   // K and V tiles of key tile j straight into their stages; rows past Sk read as zeros.
   auto issue = [&](int j) TAM_INLINE {
+    if (F16 && wave == 0) dma4(make_rsrc(a.ek + tbase + j, 4), lds0 + L::EK + (j % 3) * 256, lane * 4);
     const int row0 = j * kQBC;
     const int bytes = (Sk - row0) * D * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)row0 * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)row0 * D, bytes);
     const uint32_t kb = lds0 + L::K0 + (j % 3) * T::BYTES, vb = lds0 + L::V0 + (j & 1) * T::BYTES;
+    // the per-lane source offsets are recomputed at every issue rather than
+    // held across the loop (registers are short); the empty asm keeps the
+    // compiler from hoisting them back out
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int gi = wave * NLD + i, which = gi / T::LOADS, li = gi % T::LOADS;
-      dma16(which == 0 ? rk : rv, (which == 0 ? kb : vb) + li * 1024, loff[i]);
+      dma16(which == 0 ? rk : rv, (which == 0 ? kb : vb) + li * 1024, T::load_src(li, ln));
     }
   };
 
@@ -981,7 +1089,9 @@ void attn_bwd_dq_kernel(DqArgs a) {
   // S^T = K Q^T (P role) or dP^T = V dO^T (dS role) from the tile at roff:
   // lane holds keys 32kb + 8(v/4) + 4half + v%4 of row qrow. Skipped (zero)
   // for a tile no row of the pair sees.
-  auto scores = [&](bool active, f32x16 (&x)[2]) TAM_INLINE {
+  // (fp16 kernels: the P role's products, with K, run in fp16.)
+  auto scores = [&](auto prole_tag, bool active, f32x16 (&x)[2]) TAM_INLINE {
+    using Op = std::conditional_t<F16 && decltype(prole_tag)::value, f16x8, bf16x8>;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) x[kb] = f32x16{};
     if (!active) return;
@@ -989,25 +1099,31 @@ void attn_bwd_dq_kernel(DqArgs a) {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        x[kb] = mfma32(*reinterpret_cast<const bf16x8*>(smem + roff[ks] + kb * 32 * T::ROW_BYTES), xf[ks], x[kb]);
+        x[kb] = mfma32(*reinterpret_cast<const Op*>(smem + roff[ks] + kb * 32 * T::ROW_BYTES),
+                       __builtin_bit_cast(Op, xf[ks]), x[kb]);
   };
   // K^T rows kb*32 + k2*16 .. +15 of the tile at toff as A operands, read transposed
-  auto kt_operands = [&](int kb, int k2, bf16x8 (&a_k)[DB]) TAM_INLINE {
+  auto kt_operands = [&](int kb, int k2, KOp (&a_k)[DB]) TAM_INLINE {
     const int ro = (kb * 32 + k2 * 16) * T::ROW_BYTES;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      a_k[db] = lds_read_tr_pair(reinterpret_cast<const uint16_t*>(smem + ro + toff[db][0]),
-                                 reinterpret_cast<const uint16_t*>(smem + ro + toff[db][1]));
+      a_k[db] = __builtin_bit_cast(KOp, lds_read_tr_pair(reinterpret_cast<const uint16_t*>(smem + ro + toff[db][0]),
+                                                         reinterpret_cast<const uint16_t*>(smem + ro + toff[db][1])));
   };
 
   // P role, one tile: P = exp2(S c - lse2) with the tile's mask, handed to the
   // partner (with dropout: the sign carries the keep bit), and as bf16 B
   // operands (before dropout) for P K.
-  auto probabilities = [&](auto masked_tag, int j, bool active, const f32x16 (&x)[2],
-                           bf16x8 (&ph)[2][2]) TAM_INLINE {
+  // (fp16 kernels: with the tile's scales, P W / s_K as fp16 pairs, to the
+  // partner as well.)
+  auto probabilities = [&](auto masked_tag, int j, bool active, const f32x16 (&x)[2], int ekj,
+                           KOp (&ph)[2][2]) TAM_INLINE {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int kv0 = j * kQBC;
     float* pb = pb_at(j);
+    // c' = c / (s_K s_Q) and log2(W / s_K) of this tile
+    const float cq = F16 ? __builtin_ldexpf(c, ekj + e_blk - 28) : c;
+    const float arg0 = F16 ? (float)(15 - E_K + ekj) - rowval : -rowval;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float pf[16];
@@ -1022,7 +1138,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
                                               a.drop.seed_hi));
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float e = fast_exp2(fmaf(x[kb][v], c, -rowval));
+        float e = fast_exp2(fmaf(x[kb][v], cq, arg0));
         if (MASKED) {
           const int kv = kv0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
           const bool ok = active & (kv < Sk) & (!CAUSAL | (kv <= qrow + dlt));  // branch-free
@@ -1031,23 +1147,34 @@ void attn_bwd_dq_kernel(DqArgs a) {
         pf[v] = e;
         if (DROP) {
           pb[(16 * kb + v) * 64] = drop_keep(dwords[v >> 2], v & 3, a.drop.t) ? e : -e;
-        } else {
+        } else if (!F16) {
           pb[(16 * kb + v) * 64] = e;
         }
       }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) ph[kb][k2] = pack_bf16x8(pf + 8 * k2);
+      for (int k2 = 0; k2 < 2; ++k2) {
+        if constexpr (F16) {
+          // dword w of (kb, k2) holds keys 8 k2 + 2w and 8 k2 + 2w + 1 of block kb
+          ph[kb][k2] = pack_f16x8(pf + 8 * k2);
+          const u32x4 w4 = __builtin_bit_cast(u32x4, ph[kb][k2]);
+          uint32_t* pw = reinterpret_cast<uint32_t*>(pb);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pw[(8 * kb + 4 * k2 + w) * 64] = w4[w];
+        } else {
+          ph[kb][k2] = pack_bf16x8(pf + 8 * k2);
+        }
+      }
     }
   };
   // (P K)^T += K^T P^T. It runs for every tile (an inactive one adds exact
   // zeros) and appears once in the loop, so that each accumulator value feeds
   // one matrix instruction and is updated in place.
-  auto pk_product = [&](const bf16x8 (&ph)[2][2]) TAM_INLINE {
+  auto pk_product = [&](const KOp (&ph)[2][2]) TAM_INLINE {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        bf16x8 a_k[DB];
+        KOp a_k[DB];
         kt_operands(kb, k2, a_k);
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], ph[kb][k2], acc[db]);
@@ -1057,29 +1184,53 @@ void attn_bwd_dq_kernel(DqArgs a) {
   // dS role, second half of tile j: dS~ = P (dP - Delta~) from the partner's
   // P and the dP held since the step before, c += sum dS~, and dQ^T +=
   // K^T dS~^T with hi and lo parts (once per loop body, for every tile).
-  auto ds_tile = [&](int j, const f32x16 (&x)[2]) TAM_INLINE {
+  // (fp16 kernels: P arrives as P W / s_K, and P W/s_K (dP - Delta~) kap with
+  // kap = U / W is dS~ U / s_K, one fp16 operand; c adds it times s_K / U.)
+  // (the dS role's rowval then holds Delta~ kap, an exact power-of-two multiple)
+  const float kap = F16 ? pow2i(-1 - kLog2D - e_blk - E_V) : 1.f;
+  if (F16 && !prole) rowval *= kap;
+  auto ds_tile = [&](int j, const f32x16 (&x)[2], int ekj) TAM_INLINE {
     const float* pb = pb_at(j);
+    const float fj = F16 ? pow2i(-14 - ekj + kLog2D + e_blk + E_V + E_K) : 1.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float ds[16];
+      float tsum = 0.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float pv = pb[(16 * kb + v) * 64];
-        ds[v] = DROP ? fabsf(pv) * ((__builtin_signbit(pv) ? 0.f : a.drop.r) * x[kb][v] - rowval)
-                     : pv * (x[kb][v] - rowval);
-        csum += ds[v];
+        if constexpr (F16) {
+          const uint32_t w = reinterpret_cast<const uint32_t*>(pb)[(8 * kb + 4 * (v >> 3) + ((v & 7) >> 1)) * 64];
+          const float pv = (float)__builtin_bit_cast(f16x2, w)[v & 1];
+          ds[v] = fmaf(pv, fmaf(x[kb][v], kap, -rowval), 0.f);
+        } else {
+          const float pv = pb[(16 * kb + v) * 64];
+          ds[v] = DROP ? fabsf(pv) * ((__builtin_signbit(pv) ? 0.f : a.drop.r) * x[kb][v] - rowval)
+                       : pv * (x[kb][v] - rowval);
+        }
+        if constexpr (F16)
+          tsum += ds[v];
+        else
+          csum += ds[v];
       }
-      bf16x8 dh[2], dl[2];
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) split_bf16x8(ds + 8 * k2, &dh[k2], &dl[k2]);
+      if constexpr (F16) csum = fmaf(tsum, fj, csum);
+      KOp dh[2], dl[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        bf16x8 a_k[DB];
+        if constexpr (F16)
+          dh[k2] = pack_f16x8(ds + 8 * k2);
+        else
+          split_bf16x8(ds + 8 * k2, &dh[k2], &dl[k2]);
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        KOp a_k[DB];
         kt_operands(kb, k2, a_k);
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], dh[k2], acc[db]);
+        if constexpr (!F16) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], dl[k2], acc[db]);
+          for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], dl[k2], acc[db]);
+        }
       }
     }
   };
@@ -1097,15 +1248,16 @@ void attn_bwd_dq_kernel(DqArgs a) {
     __syncthreads();
     if (prole) {
       for (int j = 0; j < ntiles; ++j) {
+        const int ekj = F16 ? tile_exp(j) : 0;  // loaded with tile j, before the barrier
         if (j + 1 < ntiles) issue(j + 1);
         const bool active = active_at(j);
         f32x16 x[2];
-        scores(active, x);
-        bf16x8 ph[2][2];
+        scores(std::true_type{}, active, x);
+        KOp ph[2][2];
         if (masked_at(j))
-          probabilities(std::true_type{}, j, active, x, ph);
+          probabilities(std::true_type{}, j, active, x, ekj, ph);
         else
-          probabilities(std::false_type{}, j, active, x, ph);
+          probabilities(std::false_type{}, j, active, x, ekj, ph);
         pk_product(ph);
         move_roff(k_next(j));
         move_toff(k_next(j));
@@ -1115,21 +1267,24 @@ void attn_bwd_dq_kernel(DqArgs a) {
       __syncthreads();  // the partner's last phase
     } else {
       f32x16 x[2];  // dP of the tile before, carried over the barrier
+      int ek_prev = F16 ? tile_exp(0) : 0;  // that tile's exponent (fp16 kernels)
       if (ntiles > 1) issue(1);
-      scores(active_at(0), x);
+      scores(std::false_type{}, active_at(0), x);
       move_roff(v_next(0));
       wait_loads();
       __syncthreads();
       for (int j = 1; j < ntiles; ++j) {
-        ds_tile(j - 1, x);
+        const int ek_cur = F16 ? tile_exp(j) : 0;
+        ds_tile(j - 1, x, ek_prev);
         if (j + 1 < ntiles) issue(j + 1);  // after the products: its issue stalls overlap them
         move_toff(k_next(j - 1));
-        scores(active_at(j), x);
+        scores(std::false_type{}, active_at(j), x);
         move_roff(v_next(j));
+        ek_prev = ek_cur;
         wait_loads();
         __syncthreads();
       }
-      ds_tile(ntiles - 1, x);
+      ds_tile(ntiles - 1, x, ek_prev);
       __syncthreads();
     }
   }
@@ -1163,6 +1318,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
   }
   __syncthreads();
   if (prole) return;
+  if (F16) rowval *= pow2i(1 + kLog2D + e_blk + E_V);  // Delta~ again
   const float corr = sum_halves(csum);  // Delta_i - Delta~_i
   if (a.edl) {
     const float dm = wave_max(qrow < Sq ? fabsf(rowval + corr) : 0.f);
@@ -1174,7 +1330,16 @@ void attn_bwd_dq_kernel(DqArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[db][v] = a.scale * fmaf(-corr, hand[(16 * db + v) * 64], acc[db][v]);
+      for (int v = 0; v < 16; ++v) {
+        if constexpr (F16) {
+          // scale (acc / U - c P K / W)
+          const float s1 = a.scale * __builtin_ldexpf(1.f, -28 + kLog2D + e_blk + E_V + E_K);
+          const float s2 = a.scale * corr * __builtin_ldexpf(1.f, E_K - 29);
+          acc[db][v] = fmaf(-s2, hand[(16 * db + v) * 64], s1 * acc[db][v]);
+        } else {
+          acc[db][v] = a.scale * fmaf(-corr, hand[(16 * db + v) * 64], acc[db][v]);
+        }
+      }
     if (a.rope_inv) {
       // back to the unrotated queries: the partner d + D/2 of column d sits in
       // block db + DB/2 of this lane
@@ -1244,8 +1409,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_end_kernel(const float* 
 // ---------------------------------------------------------------------------
 struct Ws {
   float *delta, *lse2, *csum, *acc_dq, *acc_pk, *part;
-  uint16_t *q16, *do16;
-  int *eq, *edo, *edl;
+  uint16_t *q16, *do16, *k16;
+  int *eq, *edo, *edl, *ek, *ev;
   WsLayout w;
   Ws(const AttnShape& sh, void* base, bool block) : w(ws_layout(sh, block)) {
     char* b = static_cast<char*>(base);
@@ -1259,6 +1424,9 @@ struct Ws {
     eq = block ? nullptr : reinterpret_cast<int*>(b + w.eq);
     edo = block ? nullptr : reinterpret_cast<int*>(b + w.edo);
     edl = block ? nullptr : reinterpret_cast<int*>(b + w.edl);
+    k16 = block ? nullptr : reinterpret_cast<uint16_t*>(b + w.k16);
+    ek = block ? nullptr : reinterpret_cast<int*>(b + w.ek);
+    ev = block ? nullptr : reinterpret_cast<int*>(b + w.ev);
     part = reinterpret_cast<float*>(b + w.part);
   }
   // The fp16 dK/dV kernel runs on whole-sequence calls without dropout over
@@ -1298,9 +1466,12 @@ hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, 
                      const uint16_t* dout, uint16_t* dq, const Ws& ws, hipStream_t stream,
                      const uint16_t* o = nullptr, const float* lse = nullptr) {
   DqArgs a;
+  const bool f16 = dq && ws.f16(sh);
   a.q = q;
-  a.k = k;
+  a.k = f16 ? ws.k16 : k;
   a.v = v;
+  a.ek = f16 ? ws.ek : nullptr;
+  a.ev = f16 ? ws.ev : nullptr;
   a.dout = dout;
   a.delta = ws.delta;
   a.lse2 = ws.lse2;
@@ -1310,7 +1481,6 @@ hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, 
   a.acc_dq = dq ? nullptr : ws.acc_dq;
   a.acc_pk = dq ? nullptr : ws.acc_pk;
   a.acc_c = dq ? nullptr : ws.csum;
-  const bool f16 = dq && ws.f16(sh);
   a.q16 = f16 ? ws.q16 : nullptr;
   a.do16 = f16 ? ws.do16 : nullptr;
   a.eq = f16 ? ws.eq : nullptr;
@@ -1330,8 +1500,22 @@ hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, 
   a.sched.chunk = (a.sched.BH + 7) / 8;
   void* args[] = {&a};
   const void* kern = a.drop.t ? reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, true>)
+                     : f16    ? reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, false, true>)
                               : reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, false>);
   return hipLaunchKernel(kern, dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
+}
+
+// fp16 copy of K and the tile exponents of K and V, for the fp16 dQ kernel
+template <int D>
+hipError_t launch_k16(const AttnShape& sh, const uint16_t* k, const uint16_t* v, const Ws& ws, hipStream_t stream) {
+  int Sk = sh.Sk, ntile = (sh.Sk + 63) / 64;
+  const long long grid = (long long)sh.B * sh.Hkv * ntile;
+  uint16_t* k16 = ws.k16;
+  int* ek = ws.ek;
+  int* ev = ws.ev;
+  void* args[] = {(void*)&k, (void*)&v, (void*)&k16, (void*)&ek, (void*)&ev, (void*)&Sk, (void*)&ntile};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_k16_kernel<D>), dim3((unsigned)grid),
+                         dim3(kThreads), args, 0, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -1391,8 +1575,9 @@ hipError_t launch_all(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
   hipError_t e;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return e;
-  // 1. (Delta~ and lse2 are formed inside the dQ kernel on this path; the
-  //    event slot is kept so the per-kernel timing layout stays the same)
+  // 1. the fp16 copy of K for the fp16 dQ kernel (Delta~ and lse2 are formed
+  //    inside the dQ kernel on this path)
+  if (ws.f16(sh) && (e = launch_k16<D>(sh, k, v, ws, stream)) != hipSuccess) return e;
   if ((e = mark(1)) != hipSuccess) return e;
   // 2. dQ, which also writes lse2 and the exact Delta for the dK/dV kernel
   if ((e = launch_dq<D, CAUSAL>(sh, q, k, v, dout, dq, ws, stream, o, lse)) != hipSuccess ||

@@ -158,6 +158,13 @@ __device__ __forceinline__ int ceil_log2(float m) {
   return e < kMinExp ? kMinExp : e > kMaxExp ? kMaxExp : e;
 }
 
+// 2^e as a float, with e clamped to the normal range, built from the bits so
+// that a wave-uniform e keeps the result in a scalar register.
+__device__ __forceinline__ float pow2i(int e) {
+  e = e < -126 ? -126 : e > 127 ? 127 : e;
+  return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+
 // Largest magnitude among eight bf16 values, as a bf16 bit pattern (sign clear):
 // for finite values the patterns order like the magnitudes.
 __device__ __forceinline__ uint32_t bf16x8_max_mag(const bf16x8& x) {
