@@ -507,8 +507,11 @@ def main():
     # Algorithmic FLOPs each kernel carries out of the counted total: the forward
     # kernel's two products; the dK/dV kernel's recomputed S and dP plus dV and dK;
     # the dQ kernel's dQ. Executed FLOPs add the dQ kernel's second recomputation
-    # of S and dP, its exact-Delta correction product and the lo halves of the
-    # split bf16 operands (dV, dK, dQ).
+    # of S and dP and its exact-Delta correction product, and, on the bf16 path,
+    # the lo halves of the split operands (dV, dK, dQ). The library takes the fp16
+    # path (one product per gradient) for calls without dropout over 512 keys or
+    # more.
+    fp16_path = not args.dropout and w.S >= 512
     alg_flops = {
         "attn_fwd_kernel": w.fwd_flops(),
         "attn_bwd_dkdv_kernel": 2 * w.fwd_flops(),
@@ -516,8 +519,8 @@ def main():
     }
     exec_flops = {
         "attn_fwd_kernel": w.fwd_flops(),
-        "attn_bwd_dkdv_kernel": 3 * w.fwd_flops(),
-        "attn_bwd_dq_kernel": 5 * w.fwd_flops() // 2,
+        "attn_bwd_dkdv_kernel": (2 if fp16_path else 3) * w.fwd_flops(),
+        "attn_bwd_dq_kernel": (4 if fp16_path else 5) * w.fwd_flops() // 2,
     }
     kernels = {}
     for name, t in per.items():
