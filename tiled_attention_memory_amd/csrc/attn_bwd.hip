@@ -902,7 +902,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
   constexpr int DB = D / 32;
   constexpr int kLog2D = D == 128 ? 7 : 6;
   static_assert(!(F16 && DROP), "the fp16 kernels run without dropout");
-  constexpr int NLD = T::LOADS / 4;   // K and V loads per wave per tile
+  constexpr int NLD = T::LOADS / 2;   // K and V loads per P-role wave per tile
   static_assert(kQBC == T::ROWS && kQBR == 128, "tile sizes");
   static_assert(L::BYTES <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
@@ -1051,7 +1051,11 @@ void attn_bwd_dq_kernel(DqArgs a) {
     return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(smem + L::EK + (j % 3) * 256));
   };
 
-  // K and V tiles of key tile j straight into their stages; rows past Sk read as zeros.
+  // K and V tiles of key tile j straight into their stages; rows past Sk read as
+  // zeros. Only the four P-role waves call it, each issuing an eighth of the
+  // loads, so a dS-role wave has no tile loads in flight and a wait on its own
+  // loads never waits for the next tile (and the offsets take no dS-role
+  // registers).
   auto issue = [&](int j) TAM_INLINE {
     if (F16 && wave == 0) dma4(make_rsrc(a.ek + tbase + j, 4), lds0 + L::EK + (j % 3) * 256, lane * 4);
     const int row0 = j * kQBC;
@@ -1059,15 +1063,10 @@ void attn_bwd_dq_kernel(DqArgs a) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)row0 * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)row0 * D, bytes);
     const uint32_t kb = lds0 + L::K0 + (j % 3) * T::BYTES, vb = lds0 + L::V0 + (j & 1) * T::BYTES;
-    // the per-lane source offsets are recomputed at every issue rather than
-    // held across the loop (registers are short); the empty asm keeps the
-    // compiler from hoisting them back out
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int gi = wave * NLD + i, which = gi / T::LOADS, li = gi % T::LOADS;
-      dma16(which == 0 ? rk : rv, (which == 0 ? kb : vb) + li * 1024, T::load_src(li, ln));
+      dma16(which == 0 ? rk : rv, (which == 0 ? kb : vb) + li * 1024, T::load_src(li, lane));
     }
   };
 
@@ -1087,14 +1086,15 @@ void attn_bwd_dq_kernel(DqArgs a) {
   };
 
   // S^T = K Q^T (P role) or dP^T = V dO^T (dS role) from the tile at roff:
-  // lane holds keys 32kb + 8(v/4) + 4half + v%4 of row qrow. Skipped (zero)
-  // for a tile no row of the pair sees.
+  // lane holds keys 32kb + 8(v/4) + 4half + v%4 of row qrow. Computed for
+  // every tile: a tile no row of the pair sees is masked whole (P = 0, a
+  // select, so any finite product is dropped), and a branch around the
+  // products would cost a register clear of x per tile.
   // (fp16 kernels: the P role's products, with K, run in fp16.)
-  auto scores = [&](auto prole_tag, bool active, f32x16 (&x)[2]) TAM_INLINE {
+  auto scores = [&](auto prole_tag, f32x16 (&x)[2]) TAM_INLINE {
     using Op = std::conditional_t<F16 && decltype(prole_tag)::value, f16x8, bf16x8>;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) x[kb] = f32x16{};
-    if (!active) return;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -1239,20 +1239,20 @@ void attn_bwd_dq_kernel(DqArgs a) {
   // each pair runs tile t whole (S, P, P K) while its dS partner finishes tile
   // t - 1 (whose P was handed over in phase t - 1: dS, dQ) and then computes
   // dP of tile t. The two waves of a pair share a SIMD, so the exponentials of
-  // one overlap the matrix products of the other. Tile t + 1 loads meanwhile:
-  // its K stage last served tile t - 2, its V stage tile t - 1. Both roles
-  // pass ntiles + 2 barriers.
+  // one overlap the matrix products of the other. The P waves load tile t + 1
+  // meanwhile: its K stage last served tile t - 2, its V stage tile t - 1.
+  // Both roles pass ntiles + 2 barriers.
   if (ntiles > 0) {
-    issue(0);
+    if (prole) issue(0);
     wait_loads();
     __syncthreads();
     if (prole) {
       for (int j = 0; j < ntiles; ++j) {
         const int ekj = F16 ? tile_exp(j) : 0;  // loaded with tile j, before the barrier
-        if (j + 1 < ntiles) issue(j + 1);
         const bool active = active_at(j);
         f32x16 x[2];
-        scores(std::true_type{}, active, x);
+        scores(std::true_type{}, x);
+        if (j + 1 < ntiles) issue(j + 1);  // after the score products: the issue stalls overlap them
         KOp ph[2][2];
         if (masked_at(j))
           probabilities(std::true_type{}, j, active, x, ekj, ph);
@@ -1268,17 +1268,15 @@ void attn_bwd_dq_kernel(DqArgs a) {
     } else {
       f32x16 x[2];  // dP of the tile before, carried over the barrier
       int ek_prev = F16 ? tile_exp(0) : 0;  // that tile's exponent (fp16 kernels)
-      if (ntiles > 1) issue(1);
-      scores(std::false_type{}, active_at(0), x);
+      scores(std::false_type{}, x);
       move_roff(v_next(0));
       wait_loads();
       __syncthreads();
       for (int j = 1; j < ntiles; ++j) {
         const int ek_cur = F16 ? tile_exp(j) : 0;
         ds_tile(j - 1, x, ek_prev);
-        if (j + 1 < ntiles) issue(j + 1);  // after the products: its issue stalls overlap them
         move_toff(k_next(j - 1));
-        scores(std::false_type{}, active_at(j), x);
+        scores(std::false_type{}, x);
         move_roff(v_next(j));
         ek_prev = ek_cur;
         wait_loads();
