@@ -517,40 +517,21 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   const float c = a.c;
 
-  // 32-row blocks of a streamed tile that hold a pair this wave's keys see:
-  // in a masked tile, blocks entirely before the wave's keys are skipped by
-  // the score products (their probabilities are zero).
-  auto runs = [&](bool masked, int it, int qs) TAM_INLINE {
-    return !(masked && CAUSAL && it * kKBR + qs * 32 + 31 + dlt < kvb0);
-  };
-
   // x = A B^T over the head dim for the rows of the tile at rr and this
   // wave's keys: S = Q K^T (P role) or dP = dO V^T (dS role); lane holds key
   // kvrow, rows it*64 + 32qs + 8(v/4) + 4half + v%4. The two row blocks'
   // chains are interleaved (each operand read then has a product of the other
-  // chain to hide behind). In a masked tile a block entirely before the
-  // wave's keys is skipped; block 1 sees a key whenever block 0 does.
-  auto rows_by_keys = [&](auto masked_tag, int it, f32x16 (&x)[2]) TAM_INLINE {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // chain to hide behind). Both blocks run for every tile: a block entirely
+  // before the wave's keys is masked whole (P = 0 by a select, dS = 0 times a
+  // finite dP), and skipping it would cost a clear and a copy of x per step.
+  auto rows_by_keys = [&](f32x16 (&x)[2]) TAM_INLINE {
     x[0] = f32x16{};
     x[1] = f32x16{};
-    if (runs(MASKED, it, 0)) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
-          x[qs] = mfma32(*reinterpret_cast<const Op*>(smem + rr[ks] + qs * 32 * T::ROW_BYTES), kvf[ks], x[qs]);
-    } else if (runs(MASKED, it, 1)) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        x[1] = mfma32(*reinterpret_cast<const Op*>(smem + rr[ks] + 32 * T::ROW_BYTES), kvf[ks], x[1]);
-    }
-  };
-  auto rows_by_keys_at = [&](bool masked, int it, f32x16 (&x)[2]) TAM_INLINE {
-    if (masked)
-      rows_by_keys(std::true_type{}, it, x);
-    else
-      rows_by_keys(std::false_type{}, it, x);
+      for (int qs = 0; qs < 2; ++qs)
+        x[qs] = mfma32(*reinterpret_cast<const Op*>(smem + rr[ks] + qs * 32 * T::ROW_BYTES), kvf[ks], x[qs]);
   };
 
   // acc^T += A^T G for the rows of the tile at tt (read transposed) and the
@@ -588,7 +569,6 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
     float* pb = pb_at(st);
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-      const bool run = runs(masked, it, qs);
       // c' = c / (s_Q s_K) and log2(W / s_dO) of this 32-row block
       const float cq = F16 ? __builtin_ldexpf(c, ex.q[qs] + e_kv - 28) : c;
       const float lsh = F16 ? (float)(15 - E_dO + ex.d[qs]) : 0.f;
@@ -613,7 +593,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
           if (MASKED) {
             const int qrow = it * kKBR + qs * 32 + 8 * i + 4 * half + r;
             // bitwise &: every term is evaluated, so the select stays branch-free
-            const bool ok = run & (qrow < Sq) & (kvrow < Sk) & (!CAUSAL | (kvrow <= qrow + dlt));
+            const bool ok = (qrow < Sq) & (kvrow < Sk) & (!CAUSAL | (kvrow <= qrow + dlt));
             e = ok ? e : 0.f;
           }
           if (DROP) {
@@ -707,7 +687,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
         StepExp ex{};
         if constexpr (F16) ex = step_exp();  // loaded with this step's tiles, before the barrier
         f32x16 x[2];
-        rows_by_keys_at(masked, it, x);
+        rows_by_keys(x);
         if (st + 1 < nsteps) issue(st + 1, nxt);  // after the score products: the issue stalls overlap them
         Op hi[2][2], lo[2][2];
         if (masked)
@@ -728,7 +708,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
       StepExp ex_prev{};  // that step's exponents (fp16 kernels)
       if constexpr (F16) ex_prev = step_exp();
       if (nsteps > 1) issue(1, nxt);
-      rows_by_keys_at(masked_at(cur.it), cur.it, x);
+      rows_by_keys(x);
       move_rr(do_next(0));
       advance(cur);
       advance(nxt);
@@ -742,7 +722,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
         grad_scores(st - 1, x, ex_prev, hi, lo);
         accumulate(hi, lo);
         move_tt(q_next(st - 1));
-        rows_by_keys_at(masked_at(cur.it), cur.it, x);
+        rows_by_keys(x);
         move_rr(do_next(st));
         advance(cur);
         advance(nxt);
