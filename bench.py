@@ -509,9 +509,9 @@ def main():
     # the dQ kernel's dQ. Executed FLOPs add the dQ kernel's second recomputation
     # of S and dP and its exact-Delta correction product, and, on the bf16 path,
     # the lo halves of the split operands (dV, dK, dQ). The library takes the fp16
-    # path (one product per gradient) for calls without dropout over 512 keys or
-    # more.
-    fp16_path = not args.dropout and w.S >= 512
+    # path (one product per gradient) for whole-sequence calls over 512 keys or
+    # more, with or without dropout.
+    fp16_path = w.S >= 512
     alg_flops = {
         "attn_fwd_kernel": w.fwd_flops(),
         "attn_bwd_dkdv_kernel": 2 * w.fwd_flops(),

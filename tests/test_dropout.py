@@ -58,11 +58,17 @@ def test_mask_is_bit_exact(p, seed):
 
 
 CASES = [
-    # B, Hq, Hkv, S, D, causal, p
+    # B, Hq, Hkv, S, D, causal, p; up to 511 keys the backward runs the bf16
+    # hi + lo gradient products, from 512 the fp16 ones with the dropout scale
+    # folded into the power-of-two operand scales (p = 0.75: r = 4 = 2^2)
     (1, 4, 2, 200, 128, True, 0.1),
     (2, 8, 2, 333, 128, True, 0.5),
     (1, 4, 4, 129, 64, True, 0.25),
     (1, 6, 2, 190, 128, False, 0.3),
+    (1, 4, 2, 640, 128, True, 0.1),
+    (1, 4, 1, 600, 64, True, 0.5),
+    (1, 2, 2, 530, 128, False, 0.3),
+    (1, 2, 1, 520, 128, True, 0.75),
 ]
 
 

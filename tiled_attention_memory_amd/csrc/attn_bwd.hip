@@ -36,9 +36,9 @@
 //             workspace.
 //   4. reduce (only with several subsets): sums the partials in a fixed order.
 // Precision of the gradient products (P for dV, dS for dK and dQ): for short
-// sequences, dropout and the block protocol, the second operand enters the
-// bf16 MFMA as a hi + lo pair of bf16 values, about 16 significant bits.
-// Whole-sequence calls without dropout over 512 keys or more instead run every
+// sequences and the block protocol, the second operand enters the bf16 MFMA
+// as a hi + lo pair of bf16 values, about 16 significant bits. Whole-sequence
+// calls over 512 keys or more (with or without dropout) instead run every
 // product of the dK/dV kernel, and those with K in the dQ kernel (S, P K and
 // dQ), in fp16 (11 significant bits, one product each) on power-of-two scaled
 // operands: copies of Q and dO that the dQ kernel writes, and a copy of K made
@@ -319,7 +319,8 @@ struct DkdvLayout {
 // W = 2^15 min_b s_dO(b) over the unit's blocks keeps them at or below 2^15;
 // and dS goes to the dK product as dS U / s_Q(b), where U is the largest power
 // of two keeping every block's dS at or below 2^15, from the bound
-// |dS| <= |dP| + |Delta| <= D 2^(eD + eV) + 2^eDelta. dV = acc / W and
+// |dS| <= r |dP| + |Delta| <= D 2^(eD + eV + eR) + 2^eDelta (r <= 2^eR the
+// dropout scale, 1 without dropout). dV = r acc / W and
 // dK = scale acc / U at the end.
 template <int D, bool CAUSAL, bool DROP = false, bool F16 = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads), amdgpu_waves_per_eu(2, 2)))
@@ -333,7 +334,6 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   constexpr int kLog2D = D == 128 ? 7 : 6;
   static_assert(kKBR == T::ROWS && kKBC == 2 * T::ROWS, "tile sizes");
   static_assert(L::BYTES <= 160 * 1024, "LDS");
-  static_assert(!(F16 && DROP), "the fp16 kernels run without dropout");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
 
   int stream, t;
@@ -428,10 +428,12 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 
   // fp16 kernels: unit-wide exponents over the 32-row blocks the unit visits,
   // E_dO = max eD (W = 2^(29 - E_dO)) and, for the dS role,
-  // E_U = max (eQ + max(log2 D + eD + eV, eDelta)) (U = 2^(28 - E_U)).
+  // E_U = max (eQ + max(log2 D + eD + eV + eR, eDelta)) (U = 2^(28 - E_U)),
+  // with 2^eR >= r the dropout scale (eR = 0 without dropout).
   const int nblk = (Sq + 31) / 32;
   int E_dO = kMinExp, E_U = kMinExp;
   if constexpr (F16) {
+    const int eR = DROP ? ceil_log2(a.drop.r) : 0;
     const int nb = 2 * per_head;  // blocks per head: query tiles i_min .. NQ - 1
     for (int i = lane; i < nb * hps; i += 64) {
       const int hh = i / nb;
@@ -440,7 +442,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
         const size_t o = ((size_t)b * a.Hq + h_first + hh) * nblk + blk;
         const int ed = a.edo[o];
         E_dO = max(E_dO, ed);
-        if (!vrole) E_U = max(E_U, a.eq[o] + max(kLog2D + ed + e_kv, a.edl[o]));
+        if (!vrole) E_U = max(E_U, a.eq[o] + max(kLog2D + ed + e_kv + eR, a.edl[o]));
       }
     }
     E_dO = __builtin_amdgcn_readfirstlane(wave_max(E_dO));
@@ -573,6 +575,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
       const float cq = F16 ? __builtin_ldexpf(c, ex.q[qs] + e_kv - 28) : c;
       const float lsh = F16 ? (float)(15 - E_dO + ex.d[qs]) : 0.f;
       float p[16];
+      float ps[16];  // fp16 kernels with dropout: the partner's copy, sign = drop bit
       // Dropout bytes: the four lanes of a quad hold keys 4m .. 4m + 3 and need
       // the same four generator calls (row groups i = 0..3); lane 4m + j makes
       // call j, turns its words so that word n holds key n's bytes of rows
@@ -598,8 +601,14 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
           }
           if (DROP) {
             const bool keep = drop_keep(dq4[i], r, a.drop.t);
-            pb[(16 * qs + v) * 64] = keep ? e : -e;
-            p[v] = keep ? e * a.drop.r : 0.f;
+            if constexpr (F16) {
+              // r is applied to dV at the end, so the operand stays below 2^15
+              ps[v] = keep ? e : -e;
+              p[v] = keep ? e : 0.f;
+            } else {
+              pb[(16 * qs + v) * 64] = keep ? e : -e;
+              p[v] = keep ? e * a.drop.r : 0.f;
+            }
           } else {
             p[v] = e;
             if constexpr (!F16) pb[(16 * qs + v) * 64] = e;
@@ -609,10 +618,11 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         if constexpr (F16) {
-          // the partner takes the same fp16 pairs: dword w of (qs, k2) holds
-          // elements 8 k2 + 2w and 8 k2 + 2w + 1
+          // the partner takes the same fp16 pairs (with dropout, P with the
+          // drop bit as sign): dword w of (qs, k2) holds elements 8 k2 + 2w
+          // and 8 k2 + 2w + 1
           hi[qs][k2] = pack_f16x8(p + 8 * k2);
-          const u32x4 w4 = __builtin_bit_cast(u32x4, hi[qs][k2]);
+          const u32x4 w4 = __builtin_bit_cast(u32x4, DROP ? pack_f16x8(ps + 8 * k2) : hi[qs][k2]);
           uint32_t* pw = reinterpret_cast<uint32_t*>(pb);
 #pragma unroll
           for (int w = 0; w < 4; ++w) pw[(8 * qs + 4 * k2 + w) * 64] = w4[w];
@@ -636,6 +646,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
     for (int qs = 0; qs < 2; ++qs) {
       const float kap = F16 ? __builtin_ldexpf(1.f, -29 - E_U + E_dO + e_kv + ex.q[qs]) : 1.f;
       const float mu = F16 ? __builtin_ldexpf(1.f, -1 - ex.d[qs] - E_U + E_dO + ex.q[qs]) : 1.f;
+      const float kr = kap * a.drop.r;  // dropout: kept elements' dP factor
       float ds[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -647,7 +658,10 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
             // P as the partner's fp16 pair; the widening folds into the multiply
             const uint32_t w = reinterpret_cast<const uint32_t*>(pb)[(8 * qs + 4 * (v >> 3) + ((v & 7) >> 1)) * 64];
             const float pv = (float)__builtin_bit_cast(f16x2, w)[v & 1];
-            ds[v] = fmaf(pv, fmaf(x[qs][v], kap, -dl4[r] * mu), 0.f);
+            if constexpr (DROP)
+              ds[v] = fmaf(fabsf(pv), fmaf(x[qs][v], __builtin_signbit(pv) ? 0.f : kr, -dl4[r] * mu), 0.f);
+            else
+              ds[v] = fmaf(pv, fmaf(x[qs][v], kap, -dl4[r] * mu), 0.f);
           } else {
             const float pv = pb[(16 * qs + v) * 64];
             ds[v] = DROP ? fabsf(pv) * ((__builtin_signbit(pv) ? 0.f : a.drop.r) * x[qs][v] - dl4[r])
@@ -740,7 +754,8 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   // lane holds key kvrow, head-dim entries 32db + 8i + 4half + (0..3)
   if (kvrow < Sk) {
     // fp16 kernels: dV = acc / W, dK = scale acc / U
-    const float mul = F16 ? (vrole ? __builtin_ldexpf(1.f, E_dO - 29) : a.scale * __builtin_ldexpf(1.f, E_U - 28))
+    const float mul = F16 ? (vrole ? (DROP ? a.drop.r : 1.f) * __builtin_ldexpf(1.f, E_dO - 29)
+                                   : a.scale * __builtin_ldexpf(1.f, E_U - 28))
                           : (vrole ? 1.f : a.scale);
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] *= mul;
@@ -871,7 +886,8 @@ struct DqLayout {
 // unit's tiles; the dS role forms dS U / s_K(t) from it with one unit-wide
 // factor, U the largest power of two keeping every dS at or below 2^15 by
 // |dS~| <= |dP| + |Delta~| <= 2 D 2^(eD + E_V) (E_V = max ev, since O is a
-// mean of V rows). dP = V dO^T stays in bf16. dQ = scale (acc / U - c PK / W).
+// mean of V rows; with dropout both terms grow by r <= 2^eR, so E_V takes eR
+// on). dP = V dO^T stays in bf16. dQ = scale (acc / U - c PK / W).
 template <int D, bool CAUSAL, bool DROP = false, bool F16 = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(DqArgs a) {
@@ -881,7 +897,6 @@ void attn_bwd_dq_kernel(DqArgs a) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int kLog2D = D == 128 ? 7 : 6;
-  static_assert(!(F16 && DROP), "the fp16 kernels run without dropout");
   constexpr int NLD = T::LOADS / 2;   // K and V loads per P-role wave per tile
   static_assert(kQBC == T::ROWS && kQBR == 128, "tile sizes");
   static_assert(L::BYTES <= 160 * 1024, "LDS");
@@ -1026,6 +1041,8 @@ void attn_bwd_dq_kernel(DqArgs a) {
     }
     E_K = __builtin_amdgcn_readfirstlane(wave_max(E_K));
     E_V = __builtin_amdgcn_readfirstlane(wave_max(E_V));
+    // dropout scales the kept dP by r <= 2^eR: the dS scale takes it as part of E_V
+    if (DROP) E_V += ceil_log2(a.drop.r);
   }
   auto tile_exp = [&](int j) TAM_INLINE {
     return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(smem + L::EK + (j % 3) * 256));
@@ -1107,6 +1124,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float pf[16];
+      float ps[16];  // fp16 kernels with dropout: the partner's copy, sign = drop bit
       // Dropout words: the four lanes of a quad hold rows 4m .. 4m + 3 and need
       // the same four generator calls (key groups of this half); lane 4m + j
       // makes call j and the quad swaps, leaving each lane its row's word of
@@ -1125,7 +1143,9 @@ void attn_bwd_dq_kernel(DqArgs a) {
           e = ok ? e : 0.f;
         }
         pf[v] = e;
-        if (DROP) {
+        if (DROP && F16) {
+          ps[v] = drop_keep(dwords[v >> 2], v & 3, a.drop.t) ? e : -e;
+        } else if (DROP) {
           pb[(16 * kb + v) * 64] = drop_keep(dwords[v >> 2], v & 3, a.drop.t) ? e : -e;
         } else if (!F16) {
           pb[(16 * kb + v) * 64] = e;
@@ -1135,8 +1155,9 @@ void attn_bwd_dq_kernel(DqArgs a) {
       for (int k2 = 0; k2 < 2; ++k2) {
         if constexpr (F16) {
           // dword w of (kb, k2) holds keys 8 k2 + 2w and 8 k2 + 2w + 1 of block kb
+          // (with dropout, P with the drop bit as sign)
           ph[kb][k2] = pack_f16x8(pf + 8 * k2);
-          const u32x4 w4 = __builtin_bit_cast(u32x4, ph[kb][k2]);
+          const u32x4 w4 = __builtin_bit_cast(u32x4, DROP ? pack_f16x8(ps + 8 * k2) : ph[kb][k2]);
           uint32_t* pw = reinterpret_cast<uint32_t*>(pb);
 #pragma unroll
           for (int w = 0; w < 4; ++w) pw[(8 * kb + 4 * k2 + w) * 64] = w4[w];
@@ -1168,6 +1189,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
   // kap = U / W is dS~ U / s_K, one fp16 operand; c adds it times s_K / U.)
   // (the dS role's rowval then holds Delta~ kap, an exact power-of-two multiple)
   const float kap = F16 ? pow2i(-1 - kLog2D - e_blk - E_V) : 1.f;
+  const float kr = kap * a.drop.r;  // dropout: kept elements' dP factor
   if (F16 && !prole) rowval *= kap;
   auto ds_tile = [&](int j, const f32x16 (&x)[2], int ekj) TAM_INLINE {
     const float* pb = pb_at(j);
@@ -1181,7 +1203,10 @@ void attn_bwd_dq_kernel(DqArgs a) {
         if constexpr (F16) {
           const uint32_t w = reinterpret_cast<const uint32_t*>(pb)[(8 * kb + 4 * (v >> 3) + ((v & 7) >> 1)) * 64];
           const float pv = (float)__builtin_bit_cast(f16x2, w)[v & 1];
-          ds[v] = fmaf(pv, fmaf(x[kb][v], kap, -rowval), 0.f);
+          if constexpr (DROP)
+            ds[v] = fmaf(fabsf(pv), fmaf(x[kb][v], __builtin_signbit(pv) ? 0.f : kr, -rowval), 0.f);
+          else
+            ds[v] = fmaf(pv, fmaf(x[kb][v], kap, -rowval), 0.f);
         } else {
           const float pv = pb[(16 * kb + v) * 64];
           ds[v] = DROP ? fabsf(pv) * ((__builtin_signbit(pv) ? 0.f : a.drop.r) * x[kb][v] - rowval)
@@ -1407,11 +1432,11 @@ struct Ws {
     ev = block ? nullptr : reinterpret_cast<int*>(b + w.ev);
     part = reinterpret_cast<float*>(b + w.part);
   }
-  // The fp16 dK/dV kernel runs on whole-sequence calls without dropout over
-  // at least kF16MinKeys keys: below that its saving (which grows with the
-  // keys each row sees) does not repay the fp16 copies the dQ kernel writes
-  // (which grow with the rows alone).
-  bool f16(const AttnShape& sh) const { return q16 != nullptr && sh.drop_t == 0 && sh.Sk >= kF16MinKeys; }
+  // The fp16 kernels run on whole-sequence calls over at least kF16MinKeys
+  // keys: below that their saving (which grows with the keys each row sees)
+  // does not repay the fp16 copies the dQ kernel writes (which grow with the
+  // rows alone).
+  bool f16(const AttnShape& sh) const { return q16 != nullptr && sh.Sk >= kF16MinKeys; }
 };
 
 template <int D>
@@ -1477,9 +1502,10 @@ hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, 
   a.sched.NT = (sh.Sq + kQBR - 1) / kQBR;
   a.sched.chunk = (a.sched.BH + 7) / 8;
   void* args[] = {&a};
-  const void* kern = a.drop.t ? reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, true>)
-                     : f16    ? reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, false, true>)
-                              : reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, false>);
+  const void* kern = a.drop.t ? (f16 ? reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, true, true>)
+                                     : reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, true>))
+                     : f16 ? reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, false, true>)
+                           : reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL, false>);
   return hipLaunchKernel(kern, dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
 }
 
@@ -1527,9 +1553,10 @@ hipError_t launch_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k
   a.sched.NT = (sh.Sk + kKBC - 1) / kKBC;
   a.sched.chunk = (a.sched.BH + 7) / 8;
   void* args[] = {&a};
-  const void* kern = a.drop.t ? reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, true>)
-                     : f16    ? reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, false, true>)
-                              : reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, false>);
+  const void* kern = a.drop.t ? (f16 ? reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, true, true>)
+                                     : reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, true>))
+                     : f16 ? reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, false, true>)
+                           : reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL, false>);
   return hipLaunchKernel(kern, dim3((unsigned)sched_grid(a.sched)), dim3(kBwdThreads), args, 0, stream);
 }
 
