@@ -118,3 +118,25 @@ def test_zero_probability_is_plain_attention_and_seeds_matter():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert not torch.equal(o1.view(torch.int16), o.view(torch.int16))
+
+
+def test_llama2_layer_heads_with_dropout():
+    """S=4096, 64/8 heads, p = 0.1 (the fp16 backward): every element of O, LSE and
+    dQ for two query heads of kv head 3; dK and dV need all eight heads of the
+    group and are covered at this size without dropout in test_parity.py and
+    with dropout over 512 keys above."""
+    w = wl.BY_NAME["llama2_70b_layer_s4096"]
+    p, seed, kvh = 0.1, 77, 3
+    heads = [kvh * w.group + 1, kvh * w.group + 6]
+    say(f"workload {w.name} with dropout p={p}: heads {heads}")
+    x = wl.workload_inputs(w)
+    g = run(x, True, w.scale, p, seed)
+    q, do = (att.bf16_bits_to_f64(x[n][:, heads]) for n in ("q", "do"))
+    k, v = (att.bf16_bits_to_f64(x[n][:, kvh:kvh + 1]) for n in ("k", "v"))
+    rows = np.arange(w.S)
+    say("oracle on the two heads")
+    ref = dr.backward(q, k, v, do, w.scale, True, p, seed,
+                      masks=lambda b, h: dr.keep_mask(b, heads[h], w.Hq, rows, rows, p, seed))
+    for name in ("o", "dq"):
+        assert_close(name, to_f64(g[name])[:, heads], ref[name])
+    assert_lse(to_f64(g["lse"])[:, heads], ref["lse"])
