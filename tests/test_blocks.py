@@ -77,11 +77,14 @@ def run_blocks(x, causal, scale, qcuts, kcuts):
 
 
 CASES = [
-    # B, Hq, Hkv, S, D, causal, query cuts, key cuts
+    # B, Hq, Hkv, S, D, causal, query cuts, key cuts; key blocks of 1024 keys
+    # or more take the fp16 dK/dV kernel (the last two cases)
     (1, 4, 2, 700, 128, True, [300], [256, 500]),
     (1, 8, 1, 333, 128, True, [64, 200], [100]),
     (2, 4, 4, 257, 64, True, [129], [64, 190]),
     (1, 4, 2, 300, 128, False, [111], [150]),
+    (1, 4, 2, 2200, 128, True, [1000], [1100]),
+    (1, 2, 1, 2100, 64, False, [900], [1030]),
 ]
 
 

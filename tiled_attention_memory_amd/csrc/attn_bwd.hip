@@ -67,6 +67,9 @@ constexpr int kKBC = 128;   // dkdv: keys per workgroup
 constexpr int kKBR = 64;    // dkdv: query rows per streamed tile
 constexpr int kTargetUnits = 1024;
 constexpr int kF16MinKeys = 512;
+// Block protocol: a separate pass converts the query block's Q and dO for each
+// key block's dK/dV call, about twice the traffic of the dQ kernel's copies.
+constexpr int kF16MinBlockKeys = 1024;
 
 // ---------------------------------------------------------------------------
 // workspace layout
@@ -150,7 +153,9 @@ struct WsLayout {
 // kernel, the fp16 copy of K with its tile exponents (and those of V) for the
 // fp16 dQ kernel, and the dK/dV partials. Block protocol (block = true): Delta, lse2,
 // the running c = sum dS~ per row, the fp32 sums of dS~ K and P K over the key
-// blocks seen so far, and the partials.
+// blocks seen so far, the fp16 copies of Q and dO with the block exponents
+// (for the fp16 dK/dV kernel; its dQ calls keep bf16 operands), and the
+// partials.
 WsLayout ws_layout(const AttnShape& sh, bool block = false) {
   WsLayout w;
   const size_t rows = (size_t)sh.B * sh.Hq * sh.Sq;
@@ -165,14 +170,18 @@ WsLayout ws_layout(const AttnShape& sh, bool block = false) {
     w.acc_dq = w.csum + align256(rows * 4);
     w.acc_pk = w.acc_dq + align256(rows * sh.D * 4);
     off = w.acc_pk + align256(rows * sh.D * 4);
-  } else {
+  }
+  {
     w.q16 = off;
     w.do16 = w.q16 + align256(rows * sh.D * 2);
     w.eq = w.do16 + align256(rows * sh.D * 2);
     w.edo = w.eq + align256(blocks * 4);
     w.edl = w.edo + align256(blocks * 4);
+    off = w.edl + align256(blocks * 4);
+  }
+  if (!block) {
     const size_t kv_tiles = (size_t)sh.B * sh.Hkv * ((sh.Sk + 63) / 64);
-    w.k16 = w.edl + align256(blocks * 4);
+    w.k16 = off;
     w.ek = w.k16 + align256((size_t)sh.B * sh.Hkv * sh.Sk * sh.D * 2);
     w.ev = w.ek + align256(kv_tiles * 4);
     off = w.ev + align256(kv_tiles * 4);
@@ -265,6 +274,78 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_k16_kernel(const uint16_t* 
   if (tid == 0) {
     ek[head * ntile + tile] = e;
     ev[head * ntile + tile] = ceil_log2(__builtin_bit_cast(float, mv << 16));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1c. Block protocol: fp16 copies of a query block's Q and dO with the
+//     exponents of each 32-row block of Q, dO and the exact Delta, for the
+//     fp16 dK/dV kernel (on the whole-sequence path the dQ kernel writes
+//     them): block b is stored as x * 2^(14 - e(b)), e = ceil(log2 of its
+//     largest |x|). One workgroup per (batch * head, 32-row block).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_rows16_kernel(const uint16_t* q, const uint16_t* dout,
+                                                                   const float* delta, uint16_t* q16,
+                                                                   uint16_t* do16, int* eq, int* edo, int* edl,
+                                                                   int Sq, int nblk) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int NC = 32 * CPR / kThreads;    // chunks per thread
+  static_assert(NC >= 1, "chunks");
+  __shared__ uint32_t red[3][kThreads / 64];
+  const int blk = blockIdx.x % nblk;
+  const size_t bh = blockIdx.x / nblk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row0 = blk * 32;
+  const size_t base = (bh * Sq + (size_t)row0) * D;
+  const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  bf16x8 qc[NC], dc[NC];
+  uint32_t mq = 0, md = 0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = tid + kThreads * i, row = c / CPR;
+    const bool ok = row0 + row < Sq;
+    const size_t off = base + (size_t)c * 8;   // chunks of consecutive rows are contiguous
+    qc[i] = ok ? *reinterpret_cast<const bf16x8*>(q + off) : zero;
+    dc[i] = ok ? *reinterpret_cast<const bf16x8*>(dout + off) : zero;
+    const uint32_t a = bf16x8_max_mag(qc[i]), b = bf16x8_max_mag(dc[i]);
+    mq = mq > a ? mq : a;
+    md = md > b ? md : b;
+  }
+  const float dl = (tid < 32 && row0 + tid < Sq) ? fabsf(delta[bh * Sq + row0 + tid]) : 0.f;
+  mq = wave_max(mq);
+  md = wave_max(md);
+  const uint32_t ml = __builtin_bit_cast(uint32_t, wave_max(dl));   // non-negative: bits order as values
+  if (lane == 0) {
+    red[0][wave] = mq;
+    red[1][wave] = md;
+    red[2][wave] = ml;
+  }
+  __syncthreads();
+  uint32_t mlx = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    mq = mq > red[0][w] ? mq : red[0][w];
+    md = md > red[1][w] ? md : red[1][w];
+    mlx = mlx > red[2][w] ? mlx : red[2][w];
+  }
+  const int e_q = ceil_log2(__builtin_bit_cast(float, mq << 16));
+  const int e_d = ceil_log2(__builtin_bit_cast(float, md << 16));
+  const float sq = __builtin_ldexpf(1.f, 14 - e_q), sd = __builtin_ldexpf(1.f, 14 - e_d);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = tid + kThreads * i, row = c / CPR;
+    if (row0 + row < Sq) {
+      const size_t off = base + (size_t)c * 8;
+      *reinterpret_cast<f16x8*>(q16 + off) = bf16x8_to_f16x8(qc[i], sq);
+      *reinterpret_cast<f16x8*>(do16 + off) = bf16x8_to_f16x8(dc[i], sd);
+    }
+  }
+  if (tid == 0) {
+    const size_t o = bh * nblk + blk;
+    eq[o] = e_q;
+    edo[o] = e_d;
+    edl[o] = ceil_log2(__builtin_bit_cast(float, mlx));
   }
 }
 
@@ -1415,28 +1496,29 @@ struct Ws {
   uint16_t *q16, *do16, *k16;
   int *eq, *edo, *edl, *ek, *ev;
   WsLayout w;
-  Ws(const AttnShape& sh, void* base, bool block) : w(ws_layout(sh, block)) {
+  bool block;
+  Ws(const AttnShape& sh, void* base, bool block_) : w(ws_layout(sh, block_)), block(block_) {
     char* b = static_cast<char*>(base);
     delta = reinterpret_cast<float*>(b + w.delta);
     lse2 = reinterpret_cast<float*>(b + w.lse2);
     csum = block ? reinterpret_cast<float*>(b + w.csum) : nullptr;
     acc_dq = block ? reinterpret_cast<float*>(b + w.acc_dq) : nullptr;
     acc_pk = block ? reinterpret_cast<float*>(b + w.acc_pk) : nullptr;
-    q16 = block ? nullptr : reinterpret_cast<uint16_t*>(b + w.q16);
-    do16 = block ? nullptr : reinterpret_cast<uint16_t*>(b + w.do16);
-    eq = block ? nullptr : reinterpret_cast<int*>(b + w.eq);
-    edo = block ? nullptr : reinterpret_cast<int*>(b + w.edo);
-    edl = block ? nullptr : reinterpret_cast<int*>(b + w.edl);
+    q16 = reinterpret_cast<uint16_t*>(b + w.q16);
+    do16 = reinterpret_cast<uint16_t*>(b + w.do16);
+    eq = reinterpret_cast<int*>(b + w.eq);
+    edo = reinterpret_cast<int*>(b + w.edo);
+    edl = reinterpret_cast<int*>(b + w.edl);
     k16 = block ? nullptr : reinterpret_cast<uint16_t*>(b + w.k16);
     ek = block ? nullptr : reinterpret_cast<int*>(b + w.ek);
     ev = block ? nullptr : reinterpret_cast<int*>(b + w.ev);
     part = reinterpret_cast<float*>(b + w.part);
   }
-  // The fp16 kernels run on whole-sequence calls over at least kF16MinKeys
-  // keys: below that their saving (which grows with the keys each row sees)
-  // does not repay the fp16 copies the dQ kernel writes (which grow with the
-  // rows alone).
-  bool f16(const AttnShape& sh) const { return q16 != nullptr && sh.Sk >= kF16MinKeys; }
+  // The fp16 kernels run on calls over at least kF16MinKeys keys (in the
+  // block protocol: the dK/dV kernel only, from kF16MinBlockKeys keys): below
+  // that their saving (which grows with the keys each row sees) does not repay
+  // the fp16 copies of Q and dO (which grow with the rows alone).
+  bool f16(const AttnShape& sh) const { return sh.Sk >= (block ? kF16MinBlockKeys : kF16MinKeys); }
 };
 
 template <int D>
@@ -1522,6 +1604,22 @@ hipError_t launch_k16(const AttnShape& sh, const uint16_t* k, const uint16_t* v,
                          dim3(kThreads), args, 0, stream);
 }
 
+// block protocol: fp16 copies of the query block's Q and dO and the block
+// exponents of Q, dO and the exact Delta, for the fp16 dK/dV kernel
+template <int D>
+hipError_t launch_rows16(const AttnShape& sh, const uint16_t* q, const uint16_t* dout, const Ws& ws,
+                         hipStream_t stream) {
+  int Sq = sh.Sq, nblk = (sh.Sq + 31) / 32;
+  const long long grid = (long long)sh.B * sh.Hq * nblk;
+  const float* delta = ws.delta;
+  uint16_t *q16 = ws.q16, *do16 = ws.do16;
+  int *eq = ws.eq, *edo = ws.edo, *edl = ws.edl;
+  void* args[] = {(void*)&q, (void*)&dout, (void*)&delta, (void*)&q16, (void*)&do16, (void*)&eq,
+                  (void*)&edo, (void*)&edl, (void*)&Sq, (void*)&nblk};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_rows16_kernel<D>), dim3((unsigned)grid),
+                         dim3(kThreads), args, 0, stream);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const uint16_t* dout, uint16_t* dk, uint16_t* dv, const Ws& ws, hipStream_t stream) {
@@ -1603,8 +1701,8 @@ hipError_t block_begin(const AttnShape& sh, const uint16_t* o, const uint16_t* d
   const Ws ws(sh, workspace, true);
   hipError_t e = launch_prep<D>(sh, o, dout, lse, ws, stream);
   // the three accumulators are contiguous: c [rows] then the two [rows, D]
-  // sums, each padded to 256 bytes
-  if (e == hipSuccess) e = launch_fill_zero(ws.csum, (long long)((ws.w.part - ws.w.csum) / 4), stream);
+  // sums, each padded to 256 bytes (the fp16 copies follow them)
+  if (e == hipSuccess) e = launch_fill_zero(ws.csum, (long long)((ws.w.q16 - ws.w.csum) / 4), stream);
   return e;
 }
 
@@ -1629,8 +1727,11 @@ template <int D, bool CAUSAL>
 hipError_t block_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* dout, uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t stream) {
   const Ws ws(sh, workspace, true);
-  hipError_t e = launch_dkdv<D, CAUSAL>(sh, q, k, v, dout, dk, dv, ws, stream);
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  // the copies are rewritten by every call of the query block (the same values
+  // each time), so that no call depends on another having run
+  if (ws.f16(sh) && (e = launch_rows16<D>(sh, q, dout, ws, stream)) != hipSuccess) return e;
+  if ((e = launch_dkdv<D, CAUSAL>(sh, q, k, v, dout, dk, dv, ws, stream)) != hipSuccess) return e;
   return launch_reduce(sh, dk, dv, ws, stream);
 }
 
