@@ -154,8 +154,8 @@ struct WsLayout {
 // fp16 dQ kernel, and the dK/dV partials. Block protocol (block = true): Delta, lse2,
 // the running c = sum dS~ per row, the fp32 sums of dS~ K and P K over the key
 // blocks seen so far, the fp16 copies of Q and dO with the block exponents
-// (for the fp16 dK/dV kernel; its dQ calls keep bf16 operands), and the
-// partials.
+// (for the fp16 dK/dV kernel), the fp16 copy of the current key block's K
+// with the tile exponents (for the fp16 dQ kernel), and the partials.
 WsLayout ws_layout(const AttnShape& sh, bool block = false) {
   WsLayout w;
   const size_t rows = (size_t)sh.B * sh.Hq * sh.Sq;
@@ -179,7 +179,7 @@ WsLayout ws_layout(const AttnShape& sh, bool block = false) {
     w.edl = w.edo + align256(blocks * 4);
     off = w.edl + align256(blocks * 4);
   }
-  if (!block) {
+  {
     const size_t kv_tiles = (size_t)sh.B * sh.Hkv * ((sh.Sk + 63) / 64);
     w.k16 = off;
     w.ek = w.k16 + align256((size_t)sh.B * sh.Hkv * sh.Sk * sh.D * 2);
@@ -1374,15 +1374,20 @@ void attn_bwd_dq_kernel(DqArgs a) {
   }
 
   if (a.acc_dq) {
-    // accumulate mode: each role adds its own sums for this key block
+    // accumulate mode: each role adds its own sums for this key block (fp16
+    // kernels: back in absolute units first, P K = acc / W, sum dS~ K = acc / U;
+    // c is summed in absolute units already)
     if (qrow < Sq && ntiles > 0) {
       float* dst = (prole ? a.acc_pk : a.acc_dq) + q_base + (size_t)qrow * D + 4 * half;
+      const float mul = !F16 ? 1.f
+                        : prole ? __builtin_ldexpf(1.f, E_K - 29)
+                                : __builtin_ldexpf(1.f, -28 + kLog2D + e_blk + E_V + E_K);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           f32x4* p4 = reinterpret_cast<f32x4*>(dst + 32 * db + 8 * i);
-          *p4 += f32x4{acc[db][4 * i], acc[db][4 * i + 1], acc[db][4 * i + 2], acc[db][4 * i + 3]};
+          *p4 += mul * f32x4{acc[db][4 * i], acc[db][4 * i + 1], acc[db][4 * i + 2], acc[db][4 * i + 3]};
         }
       if (!prole) {
         const float cs = sum_halves(csum);
@@ -1509,13 +1514,13 @@ struct Ws {
     eq = reinterpret_cast<int*>(b + w.eq);
     edo = reinterpret_cast<int*>(b + w.edo);
     edl = reinterpret_cast<int*>(b + w.edl);
-    k16 = block ? nullptr : reinterpret_cast<uint16_t*>(b + w.k16);
-    ek = block ? nullptr : reinterpret_cast<int*>(b + w.ek);
-    ev = block ? nullptr : reinterpret_cast<int*>(b + w.ev);
+    k16 = reinterpret_cast<uint16_t*>(b + w.k16);
+    ek = reinterpret_cast<int*>(b + w.ek);
+    ev = reinterpret_cast<int*>(b + w.ev);
     part = reinterpret_cast<float*>(b + w.part);
   }
   // The fp16 kernels run on calls over at least kF16MinKeys keys (in the
-  // block protocol: the dK/dV kernel only, from kF16MinBlockKeys keys): below
+  // block protocol from kF16MinBlockKeys keys): below
   // that their saving (which grows with the keys each row sees) does not repay
   // the fp16 copies of Q and dO (which grow with the rows alone).
   bool f16(const AttnShape& sh) const { return sh.Sk >= (block ? kF16MinBlockKeys : kF16MinKeys); }
@@ -1551,7 +1556,8 @@ hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, 
                      const uint16_t* dout, uint16_t* dq, const Ws& ws, hipStream_t stream,
                      const uint16_t* o = nullptr, const float* lse = nullptr) {
   DqArgs a;
-  const bool f16 = dq && ws.f16(sh);
+  const bool f16 = ws.f16(sh);
+  const bool copies = f16 && dq;  // whole-sequence path: the fp16 copies for the dK/dV kernel
   a.q = q;
   a.k = f16 ? ws.k16 : k;
   a.v = v;
@@ -1566,11 +1572,11 @@ hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, 
   a.acc_dq = dq ? nullptr : ws.acc_dq;
   a.acc_pk = dq ? nullptr : ws.acc_pk;
   a.acc_c = dq ? nullptr : ws.csum;
-  a.q16 = f16 ? ws.q16 : nullptr;
-  a.do16 = f16 ? ws.do16 : nullptr;
-  a.eq = f16 ? ws.eq : nullptr;
-  a.edo = f16 ? ws.edo : nullptr;
-  a.edl = f16 ? ws.edl : nullptr;
+  a.q16 = copies ? ws.q16 : nullptr;
+  a.do16 = copies ? ws.do16 : nullptr;
+  a.eq = copies ? ws.eq : nullptr;
+  a.edo = copies ? ws.edo : nullptr;
+  a.edl = copies ? ws.edl : nullptr;
   a.Hq = sh.Hq;
   a.Hkv = sh.Hkv;
   a.Sq = sh.Sq;
@@ -1760,6 +1766,10 @@ hipError_t launch_bwd_block_begin(const AttnShape& sh, const uint16_t* o, const 
 hipError_t launch_bwd_block_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                const uint16_t* dout, void* workspace, hipStream_t stream) {
   const Ws ws(sh, workspace, true);
+  if (ws.f16(sh)) {
+    const hipError_t e = sh.D == 128 ? launch_k16<128>(sh, k, v, ws, stream) : launch_k16<64>(sh, k, v, ws, stream);
+    if (e != hipSuccess) return e;
+  }
   return TAM_DISPATCH(launch_dq, sh, q, k, v, dout, nullptr, ws, stream);
 }
 
