@@ -61,3 +61,25 @@ def test_dkdv_head_split_follows_balance():
     assert _head_split(1, 8, 8, 64, 128) == 1
     # more heads per group never shrinks the subsets below one head
     assert 16 % _head_split(1, 16, 1, 128, 128) == 0
+
+
+def test_block_workspace_holds_the_fp16_buffers():
+    """The block protocol's workspace: Delta, lse2 and c (fp32 rows of B*Hq*Sq), the two fp32
+    [B*Hq*Sq, D] sums, the fp16 copies of the query block's Q and dO with three int rows of
+    B*Hq*ceil(Sq/32) block exponents, the fp16 copy of a key block's K with two int rows of
+    B*Hkv*ceil(Sk/64) tile exponents, each padded to 256 bytes, then nsplit x 2 partial copies of
+    dK/dV when the head subsets number more than one (nsplit divides the group)."""
+    import tiled_attention_memory_amd as tam
+    pad = lambda n: (n + 255) // 256 * 256
+    for B, Hq, Hkv, Sq, Sk, D in [(1, 8, 1, 10240, 10240, 128), (1, 64, 8, 512, 512, 128),
+                                  (2, 4, 2, 1000, 1100, 64), (1, 32, 8, 16384, 16384, 128)]:
+        rows = B * Hq * Sq
+        base = (3 * pad(rows * 4) + 2 * pad(rows * D * 4) + 2 * pad(rows * D * 2)
+                + 3 * pad(B * Hq * ((Sq + 31) // 32) * 4)
+                + pad(B * Hkv * Sk * D * 2) + 2 * pad(B * Hkv * ((Sk + 63) // 64) * 4))
+        ws = tam.attn_bwd_block_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
+        assert ws >= base, (ws, base)
+        part = 2 * B * Hkv * Sk * D * 4
+        assert (ws - base) % part == 0, (ws, base, part)
+        n = max(1, (ws - base) // part)
+        assert (Hq // Hkv) % n == 0, n
