@@ -25,6 +25,12 @@
 //             the error that rounding O to bf16 puts into Delta. For the fp16
 //             dK/dV kernel it also writes fp16 copies of Q and dO and the
 //             block exponents of Q, dO and Delta.
+//   1b. k16:  fp16 copy of K with tile exponents (and those of V), before an
+//             fp16 dQ kernel.
+//   1c. rows16: block protocol only, before an fp16 dK/dV call: the fp16
+//             copies of the query block's Q and dO with the block exponents of
+//             Q, dO and the exact Delta (which kernel 2 writes on the
+//             whole-sequence path).
 //   3. dkdv:  key-stationary. One unit = (batch, kv head, 128-key tile, subset
 //             of the group's query heads); 8 waves in pairs own 32 keys per
 //             pair while 64-row Q/dO tiles stream through LDS. In each pair one
@@ -610,11 +616,13 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   auto rows_by_keys = [&](f32x16 (&x)[2]) TAM_INLINE {
     x[0] = f32x16{};
     x[1] = f32x16{};
+    if (!vrole) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs)
         x[qs] = mfma32(*reinterpret_cast<const Op*>(smem + rr[ks] + qs * 32 * T::ROW_BYTES), kvf[ks], x[qs]);
+    if (!vrole) __builtin_amdgcn_s_setprio(0);
   };
 
   // acc^T += A^T G for the rows of the tile at tt (read transposed) and the
@@ -625,7 +633,12 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
   // matrix instruction, so the compiler accumulates in place instead of
   // keeping a second copy of dV^T/dK^T.
   // (fp16 kernels: one product on G alone; the lo array is unused.)
+  // The dS wave runs both its product chains (dP in rows_by_keys, dK here)
+  // at raised wave priority, so that once started they issue back to back
+  // while the P wave fills the gaps with its exponentials (3% off the kernel;
+  // raising the P wave's as well made it 5% slower).
   auto accumulate = [&](const Op (&hi)[2][2], const Op (&lo)[2][2]) TAM_INLINE {
+    if (!vrole) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
@@ -638,6 +651,7 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
           acc[db] = mfma32(at, hi[qs][k2], acc[db]);
           if constexpr (!F16) acc[db] = mfma32(at, lo[qs][k2], acc[db]);
         }
+    if (!vrole) __builtin_amdgcn_s_setprio(0);
   };
 
   // P role, one step: P = exp2(S c - lse2) with the tile's mask, to the
