@@ -1177,10 +1177,11 @@ void attn_bwd_dq_kernel(DqArgs a) {
     return (j * kQBC + kQBC > Sk) || (CAUSAL && j * kQBC + kQBC - 1 > wrow0 + dlt);
   };
 
-  // The matrix-product chains of both roles run at raised wave priority, so
-  // that a wave that has started its products issues them back to back while
-  // its partner on the SIMD fills the gaps with vector work (2% off the
-  // kernel at S=4096).
+  // The dS wave's matrix-product chains (dP and dQ) run at raised wave
+  // priority, so that once started they issue back to back while the P wave
+  // on the same SIMD fills the gaps with its exponentials (7% off the kernel
+  // at S=4096; raising the P wave's chains too gained only 2%, the P wave's
+  // alone lost 4%).
   // S^T = K Q^T (P role) or dP^T = V dO^T (dS role) from the tile at roff:
   // lane holds keys 32kb + 8(v/4) + 4half + v%4 of row qrow. Computed for
   // every tile: a tile no row of the pair sees is masked whole (P = 0, a
@@ -1191,14 +1192,14 @@ void attn_bwd_dq_kernel(DqArgs a) {
     using Op = std::conditional_t<F16 && decltype(prole_tag)::value, f16x8, bf16x8>;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) x[kb] = f32x16{};
-    __builtin_amdgcn_s_setprio(1);
+    if (!decltype(prole_tag)::value) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         x[kb] = mfma32(*reinterpret_cast<const Op*>(smem + roff[ks] + kb * 32 * T::ROW_BYTES),
                        __builtin_bit_cast(Op, xf[ks]), x[kb]);
-    __builtin_amdgcn_s_setprio(0);
+    if (!decltype(prole_tag)::value) __builtin_amdgcn_s_setprio(0);
   };
   // K^T rows kb*32 + k2*16 .. +15 of the tile at toff as A operands, read transposed
   auto kt_operands = [&](int kb, int k2, KOp (&a_k)[DB]) TAM_INLINE {
@@ -1272,7 +1273,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
   // zeros) and appears once in the loop, so that each accumulator value feeds
   // one matrix instruction and is updated in place.
   auto pk_product = [&](const KOp (&ph)[2][2]) TAM_INLINE {
-    __builtin_amdgcn_s_setprio(1);
+
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1282,7 +1283,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] = mfma32(a_k[db], ph[kb][k2], acc[db]);
       }
-    __builtin_amdgcn_s_setprio(0);
+
   };
 
   // dS role, second half of tile j: dS~ = P (dP - Delta~) from the partner's
