@@ -1179,9 +1179,9 @@ void attn_bwd_dq_kernel(DqArgs a) {
 
   // The dS wave's matrix-product chains (dP and dQ) run at raised wave
   // priority, so that once started they issue back to back while the P wave
-  // on the same SIMD fills the gaps with its exponentials (7% off the kernel
-  // at S=4096; raising the P wave's chains too gained only 2%, the P wave's
-  // alone lost 4%).
+  // on the same SIMD fills the gaps with its exponentials (about 9% off the
+  // kernel at S=4096 against no raised priority; raising both waves' chains
+  // gained 2%, the P wave's alone lost 2%).
   // S^T = K Q^T (P role) or dP^T = V dO^T (dS role) from the tile at roff:
   // lane holds keys 32kb + 8(v/4) + 4half + v%4 of row qrow. Computed for
   // every tile: a tile no row of the pair sees is masked whole (P = 0, a
