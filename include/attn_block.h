@@ -80,10 +80,13 @@ int attn_merge(const float* const* o_parts, const float* const* lse_parts, int n
  *
  * o and lse are the merged results (attn_merge, or attn_fwd for one block).
  * The workspace belongs to one query block for the whole sequence of calls;
- * Sk in attn_bwd_block_workspace_bytes is the largest key block used. The
- * calls of one sequence must be ordered (one stream); each call is
- * deterministic, so the results are bitwise reproducible for a fixed order of
- * key blocks. B, Hq, Hkv, Sq, D (and scale) must be the same in every call.
+ * Sk in attn_bwd_block_workspace_bytes is the largest key block used, and the
+ * size it returns serves every call whose key block holds at most Sk keys
+ * (a shorter block may split the work more finely and need more partials
+ * than the longest one; the size covers that). The calls of one sequence
+ * must be ordered (one stream); each call is deterministic, so the results
+ * are bitwise reproducible for a fixed order of key blocks. B, Hq, Hkv, Sq, D
+ * (and scale) must be the same in every call.
  */
 int attn_bwd_block_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, size_t* bytes);
 

@@ -213,6 +213,30 @@ def test_block_backward_rejects():
                                    0, 0, 0.1, None) == 6    # workspace sized for a smaller key block
 
 
+@pytest.mark.parametrize("shape", [
+    # B, Hq, Hkv, Sq, largest key block, D: shapes where a shorter key block splits
+    # the group's heads more finely than the longest one
+    (1, 64, 8, 4096, 16384, 128),
+    (1, 8, 1, 10240, 131072, 128),
+    (1, 4, 2, 64, 96, 128),
+])
+def test_block_workspace_covers_every_shorter_key_block(shape):
+    """The size for the largest key block passes the workspace check of every call with a
+    shorter one. dk and dv overlap in these calls, an error checked after the workspace,
+    so a call that passes the workspace check returns ATTN_ERR_ALIAS and launches nothing."""
+    lib = tam.load()
+    B, Hq, Hkv, Sq, Sk_max, D = shape
+    need = tam.attn_bwd_block_workspace_bytes(B, Hq, Hkv, Sq, Sk_max, D)
+    W = 1 << 44
+    for sk in sorted({1, 63, 64, 127, 128, 129, 1000, 1024, 4096, 8192, 10240, Sk_max - 1, Sk_max}):
+        if sk > Sk_max:
+            continue
+        assert lib.attn_bwd_block_dkdv(A, 2 * A, 3 * A, 4 * A, 5 * A, 5 * A, W, need, B, Hq, Hkv, Sq, sk, D, 1,
+                                       0, 0, 0.1, None) == 9, sk
+        assert lib.attn_bwd_block_dq(A, 2 * A, 3 * A, 4 * A, A + 256, need, B, Hq, Hkv, Sq, sk, D, 1, 0, 0, 0.1,
+                                     None) == 9, sk
+
+
 # ---------------------------------------------------------------------------
 # decode (attn_decode.h): validation only
 # ---------------------------------------------------------------------------

@@ -263,7 +263,7 @@ ATTN_EXPORT int attn_bwd_block_workspace_bytes(int B, int Hq, int Hkv, int Sq, i
   if (!bytes) return ATTN_ERR_NULL_POINTER;
   const int st = check_shape(B, Hq, Hkv, Sq, Sk, D);
   if (st != ATTN_OK) return st;
-  *bytes = tam::bwd_block_workspace_bytes(block_shape(B, Hq, Hkv, Sq, Sk, D, 1, 0, 0, 1.f));
+  *bytes = tam::bwd_block_workspace_bytes_upto(block_shape(B, Hq, Hkv, Sq, Sk, D, 1, 0, 0, 1.f));
   return ATTN_OK;
 }
 

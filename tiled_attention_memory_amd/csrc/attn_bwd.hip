@@ -1771,6 +1771,25 @@ hipError_t block_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
 size_t bwd_workspace_bytes(const AttnShape& sh) { return ws_layout(sh).total; }
 size_t bwd_block_workspace_bytes(const AttnShape& sh) { return ws_layout(sh, true).total; }
 
+// A block call of a shorter key block can choose a larger head split, whose
+// partials then outgrow those of the longest block, so the size that serves
+// every call of a query block is the largest need over every key-block length
+// up to sh.Sk. The need depends on the length through the number of 128-key
+// tiles (which sets the split) and grows with the length at a fixed split; once
+// the tiles alone give enough units the split is 1 and the longest block needs
+// the most.
+size_t bwd_block_workspace_bytes_upto(const AttnShape& sh) {
+  const long long per_tile = (long long)sh.B * sh.Hkv;
+  const int nt = (sh.Sk + kKBC - 1) / kKBC;
+  size_t need = ws_layout(sh, true).total;
+  for (int t = 1; t < nt && per_tile * t < kTargetUnits; ++t) {
+    AttnShape s = sh;
+    s.Sk = t * kKBC;
+    need = std::max(need, ws_layout(s, true).total);
+  }
+  return need;
+}
+
 #define TAM_DISPATCH(F, ...)                                                              \
   (sh.D == 128 ? (sh.causal ? F<128, true>(__VA_ARGS__) : F<128, false>(__VA_ARGS__))   \
                : (sh.causal ? F<64, true>(__VA_ARGS__) : F<64, false>(__VA_ARGS__)))

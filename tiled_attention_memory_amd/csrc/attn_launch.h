@@ -69,7 +69,10 @@ hipError_t launch_bwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
                       hipEvent_t* events = nullptr);
 
 // Block protocol of the backward pass (one query block, key blocks in turn).
+// The need of one block call with sh.Sk keys, and the size that covers every
+// call with a key block of at most sh.Sk keys.
 size_t bwd_block_workspace_bytes(const AttnShape& sh);
+size_t bwd_block_workspace_bytes_upto(const AttnShape& sh);
 hipError_t launch_bwd_block_begin(const AttnShape& sh, const uint16_t* o, const uint16_t* dout, const float* lse,
                                   void* workspace, hipStream_t stream);
 hipError_t launch_bwd_block_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
