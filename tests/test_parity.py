@@ -6,18 +6,23 @@ O, dQ, dK, dV; |err| <= 1e-3 on the fp32 LSE.
 Small shapes are compared element by element in full; they span several tiles
 and ragged tails (S not a multiple of the 64/128-row tiles), GQA group sizes
 1..16, both head dims, causal and not. The five named workloads run at their
-full sizes in the same launch configuration the bench times; the two that the
-oracle cannot materialise in seconds (S = 32768 and 81920) are compared on
-sampled outputs the oracle computes one by one: whole query-row blocks of O,
-LSE and dQ, and whole key-row blocks of dK and dV near the end of the
-sequence (the only key rows whose exact gradients need a bounded number of
-query rows), plus the shift-invariance sums over every key row.
+full sizes in the same launch configuration the bench times:
+  * S = 256 and the batch-16 S = 64 workload: every element;
+  * S = 4096 (64/8 heads): every element of all eight GQA groups;
+  * S = 32768 (K x 3): one whole GQA group element by element (every row of
+    O, LSE, dQ of its four query heads, every key row of dK, dV);
+  * S = 81920 (8/1 heads): every row of O, LSE and dQ, and dK, dV on eight
+    whole 128-key blocks (first, last, six seeded), which the oracle computes
+    exactly from every row's LSE and Delta;
+plus, for the two long ones, the shift-invariance sums over every key row.
+The oracle runs in threads over heads and row panels (oracle_par).
 """
 import math
 
 import numpy as np
 import pytest
 
+import oracle_par as par
 from gpu_helpers import assert_close, assert_lse, run_gpu, say, to_f64
 from oracle import attention as att
 from tiled_attention_memory_amd import workloads as wl
@@ -69,54 +74,21 @@ def test_workload_full(w):
     compare_full(gpu, oracle_full(x, w.scale, True))
 
 
-def test_workload_llama2_layer_groups():
-    """S=4096, 64/8 heads: every element of two whole GQA groups (16 query heads, 2 kv heads)."""
+def test_workload_llama2_layer_all_groups():
+    """S=4096, 64/8 heads: every element of every output (all 8 GQA groups)."""
     w = wl.BY_NAME["llama2_70b_layer_s4096"]
-    say(f"workload {w.name}: groups 0 and 5")
+    say(f"workload {w.name}: all 8 groups")
     x = wl.workload_inputs(w)
     gpu = run_gpu(x, True, w.scale)
-    groups = [(0, 0), (0, 5)]
-    ref = oracle_full(x, w.scale, True, heads=groups)
-    g = w.group
-    for b, kvh in groups:
-        hs = slice(kvh * g, (kvh + 1) * g)
-        compare_full(gpu, ref, sel_q=(b, hs), sel_kv=(b, kvh))
-
-
-def sampled_check(w, gpu, x, kvh, heads, n_row_blocks, tail_keys, seed):
-    """Rows and key blocks of one GQA group at full sequence length."""
-    S, g = w.S, w.group
-    rng = np.random.default_rng(seed)
-    blocks = sorted({0, S // 128 - 1, *rng.choice(S // 128, n_row_blocks - 2, replace=False)})
-    rows = np.concatenate([np.arange(128 * i, 128 * i + 128) for i in blocks])
-    k = att.bf16_bits_to_f64(x["k"][0, kvh])
-    v = att.bf16_bits_to_f64(x["v"][0, kvh])
-    got = {n: to_f64(gpu[n][0]) for n in ("o", "dq", "lse")}
-
-    def per_rows(h, rr):
-        q = att.bf16_bits_to_f64(x["q"][0, h])
-        do = att.bf16_bits_to_f64(x["do"][0, h])
-        parts = [att.rows_forward_backward(q, k, v, do, rr[i:i + 256], w.scale)
-                 for i in range(0, len(rr), 256)]
-        return {n: np.concatenate([p[n] for p in parts]) for n in parts[0]}
-
-    for h in heads:
-        ref = per_rows(h, rows)
-        assert_close(f"o[h{h}]", got["o"][h, rows], ref["o"])
-        assert_close(f"dq[h{h}]", got["dq"][h, rows], ref["dq"])
-        assert_lse(got["lse"][h, rows], ref["lse"])
-    # key blocks inside the last tail_keys keys: their gradients need rows >= row_lo only
-    row_lo = S - tail_keys
-    cols = np.unique(np.concatenate([np.arange(row_lo, row_lo + 128), np.arange(S - 128, S)]))
-    group = list(range(kvh * g, (kvh + 1) * g))
-    rr = np.arange(row_lo, S)
-    per = [per_rows(h, rr) for h in group]
-    q_g = np.stack([att.bf16_bits_to_f64(x["q"][0, h, row_lo:]) for h in group])
-    do_g = np.stack([att.bf16_bits_to_f64(x["do"][0, h, row_lo:]) for h in group])
-    dk, dv = att.cols_dkdv(q_g, do_g, k, v, cols, np.stack([p["lse"] for p in per]),
-                           np.stack([p["delta"] for p in per]), row_lo, w.scale)
-    assert_close("dk[tail]", to_f64(gpu["dk"][0, kvh])[cols], dk)
-    assert_close("dv[tail]", to_f64(gpu["dv"][0, kvh])[cols], dv)
+    q, k, v, do = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    got = {n: to_f64(gpu[n]) for n in ("o", "lse", "dq", "dk", "dv")}
+    del gpu
+    refs = par.groups_backward(q, k, v, do, w.scale, True, [(0, kvh) for kvh in range(w.Hkv)])
+    for n in ("o", "dq"):
+        assert_close(n, got[n][0], np.concatenate([r[n] for r in refs]))
+    assert_lse(got["lse"][0], np.concatenate([r["lse"] for r in refs]))
+    for n in ("dk", "dv"):
+        assert_close(n, got[n][0], np.stack([r[n] for r in refs]))
 
 
 def shift_sums(w, gpu, x):
@@ -134,15 +106,57 @@ def shift_sums(w, gpu, x):
     assert np.max(np.abs(dv - do)) <= tol, np.max(np.abs(dv - do))
 
 
-@pytest.mark.parametrize("name,kvh,heads,tail", [
-    ("long_context_s32768_k3", 5, (20, 23), 512),
-    ("very_long_s81920", 0, (0, 6), 256),
-])
-def test_workload_long_sampled(name, kvh, heads, tail):
-    w = wl.BY_NAME[name]
-    say(f"workload {name}: sampled rows of heads {heads}, last {tail} keys of kv head {kvh}")
+def test_workload_long_context_whole_group():
+    """S=32768 with K x 3: one whole GQA group element by element -- every row of O, LSE
+    and dQ of its 4 query heads and every key row of dK, dV of its key/value head --
+    plus the shift-invariance sums over all groups."""
+    w = wl.BY_NAME["long_context_s32768_k3"]
+    kvh = 5
+    say(f"workload {w.name}: whole group of kv head {kvh}")
     x = wl.workload_inputs(w)
     gpu = run_gpu(x, True, w.scale)
-    say(f"workload {name}: oracle on samples")
-    sampled_check(w, gpu, x, kvh, heads, n_row_blocks=4, tail_keys=tail, seed=w.cfg_id)
+    g = w.group
+    hs = slice(kvh * g, (kvh + 1) * g)
+    got = {n: to_f64(gpu[n][0, hs]) for n in ("o", "lse", "dq")}
+    got.update({n: to_f64(gpu[n][0, kvh]) for n in ("dk", "dv")})
     shift_sums(w, gpu, x)
+    del gpu
+    q, k, v, do = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    say(f"workload {w.name}: oracle on the group")
+    ref, = par.groups_backward(q, k, v, do, w.scale, True, [(0, kvh)], panel_rows=1024)
+    for n in ("o", "dq", "dk", "dv"):
+        assert_close(n, got[n], ref[n])
+    assert_lse(got["lse"], ref["lse"])
+
+
+def seeded_blocks(n_blocks, n_total, seed):
+    """Block indices: the first, the last and n_blocks - 2 seeded others (sorted, distinct)."""
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, n_total - 1), n_blocks - 2, replace=False)
+    return sorted({0, n_total - 1, *(int(i) for i in mid)})
+
+
+def test_workload_very_long_rows_and_key_blocks():
+    """S=81920, 8/1 heads: every row of O, LSE and dQ of all 8 query heads, and dK, dV on
+    eight whole 128-key blocks (the first, the last and six seeded ones); the first block
+    sees every query row, so it carries the longest accumulation."""
+    w = wl.BY_NAME["very_long_s81920"]
+    say(f"workload {w.name}: all rows, 8 key blocks")
+    x = wl.workload_inputs(w)
+    gpu = run_gpu(x, True, w.scale)
+    got = {n: to_f64(gpu[n][0]) for n in ("o", "lse", "dq")}
+    blocks = seeded_blocks(8, w.S // 128, seed=w.cfg_id)
+    cols = np.concatenate([np.arange(128 * j, 128 * j + 128) for j in blocks])
+    got.update({n: to_f64(gpu[n][0, 0])[cols] for n in ("dk", "dv")})
+    shift_sums(w, gpu, x)
+    del gpu
+    q, k, v, do = (att.bf16_bits_to_f64(x[n][0]) for n in ("q", "k", "v", "do"))
+    say(f"workload {w.name}: oracle rows")
+    ref = par.all_rows(q, k[0], v[0], do, w.scale, panel_rows=512)
+    for n in ("o", "dq"):
+        assert_close(n, got[n], ref[n])
+    assert_lse(got["lse"], ref["lse"])
+    say(f"workload {w.name}: oracle key blocks {blocks}")
+    kb = par.key_blocks_dkdv(q, do, k[0], v[0], ref["lse"], ref["delta"], blocks, 128, w.scale)
+    for n, i in (("dk", 0), ("dv", 1)):
+        assert_close(f"{n}[blocks]", got[n], np.concatenate([kb[j][i] for j in blocks]))

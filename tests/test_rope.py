@@ -2,7 +2,9 @@
 
 Expected values come from oracle.rope: fp64 rotation with the rotated Q and K
 rounded to bf16 (the precision of the attention inputs), the plain attention
-oracle on the rotated pair, gradients rotated back.
+oracle on the rotated pair, gradients rotated back. The same outputs are also
+held against the plain fp64 rotation with no rounding of the rotated pair, at
+the same tolerances: the rounding reading must not hide an error beyond them.
 """
 import math
 
@@ -50,10 +52,12 @@ def test_rope_against_oracle(case):
     scale = 1.0 / math.sqrt(D)
     g = run(x, causal, scale, base)
     q, k, v, do = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v", "do"))
-    ref = rope.backward(q, k, v, do, scale, causal, base)
-    for name in ("o", "dq", "dk", "dv"):
-        assert_close(name, to_f64(g[name]), ref[name])
-    assert_lse(to_f64(g["lse"]), ref["lse"])
+    for rounded in (True, False):
+        print(f"  against the oracle with the rotated pair {'rounded to bf16' if rounded else 'in fp64'}")
+        ref = rope.backward(q, k, v, do, scale, causal, base, bf16_rotated=rounded)
+        for name in ("o", "dq", "dk", "dv"):
+            assert_close(name, to_f64(g[name]), ref[name])
+        assert_lse(to_f64(g["lse"]), ref["lse"])
 
 
 def test_rope_at_long_positions_sampled():
@@ -73,13 +77,15 @@ def test_rope_at_long_positions_sampled():
     torch.cuda.synchronize()
     qh, kh, vh = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v"))
     pos = np.arange(S)
-    kr = rope.round_bf16(rope.rotate(kh[0, 0], pos, 1e6))
     rows = np.concatenate([np.arange(0, 32), np.arange(S - 64, S), np.random.default_rng(5).choice(S, 32)])
     go, gl = to_f64(o), to_f64(lse)
-    for h in (0, 3):
-        qr = rope.round_bf16(rope.rotate(qh[0, h][rows], rows, 1e6))
-        s = w.scale * (qr @ kr.T)
-        s = np.where(np.arange(S)[None, :] <= rows[:, None], s, -np.inf)
-        p, l = att.softmax_rows(s)
-        assert_close(f"o rows h{h}", go[0, h, rows], p @ vh[0, 0])
-        assert_lse(gl[0, h, rows], l)
+    for rounded in (True, False):
+        rnd = rope.round_bf16 if rounded else (lambda a: a)
+        kr = rnd(rope.rotate(kh[0, 0], pos, 1e6))
+        for h in (0, 3):
+            qr = rnd(rope.rotate(qh[0, h][rows], rows, 1e6))
+            s = w.scale * (qr @ kr.T)
+            s = np.where(np.arange(S)[None, :] <= rows[:, None], s, -np.inf)
+            p, l = att.softmax_rows(s)
+            assert_close(f"o rows h{h} ({'bf16' if rounded else 'fp64'} rotation)", go[0, h, rows], p @ vh[0, 0])
+            assert_lse(gl[0, h, rows], l)
