@@ -78,8 +78,14 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              hipStream_t stream);
 
 /*
- * Size in bytes of the device workspace attn_bwd needs for these sizes
- * (per-row softmax terms of the backward pass). Writes it to *bytes.
+ * Size in bytes of the device workspace attn_bwd needs for these sizes. Writes
+ * it to *bytes. The workspace holds, per query row, the row term Delta and the
+ * LSE in base 2 (fp32); fp16 copies of Q, dO and K scaled by powers of two,
+ * with one exponent per 32-row block of Q and dO (and of Delta) and per
+ * 64-key tile of K and V; and, when the query heads of a group are split into
+ * subsets for load balance, fp32 dK/dV partials of each subset. Examples:
+ * B=1, Hq=64, Hkv=8, S=4096, D=128 needs 202 MiB; B=1, Hq=8, Hkv=1, S=81920,
+ * D=128 needs 665 MiB.
  * Returns ATTN_OK, ATTN_ERR_NULL_POINTER (bytes NULL), ATTN_ERR_BAD_SHAPE or
  * ATTN_ERR_UNSUPPORTED_HEAD_DIM.
  */
@@ -100,10 +106,17 @@ int attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes
  *                      and on return are unspecified.
  * dK and dV are accumulated without atomics; the results are bitwise
  * reproducible for the same inputs and sizes. The row term Delta is made
- * exact inside the pass (not taken from the rounded o alone), and the
- * probabilities and their gradients enter the bf16 matrix products as hi + lo
- * bf16 pairs, so the gradients carry fp32-class accuracy up to the final
- * bf16 rounding.
+ * exact inside the pass (not taken from the rounded o alone).
+ * Precision of the matrix products (every one accumulates in fp32; the
+ * outputs are rounded to bf16 once, at the end):
+ *   S >= 512: every product of the dK/dV kernel (S, dP, dV, dK) and the dQ
+ *     kernel's products with K (S, P K and dQ) run on fp16 operands (11
+ *     significant bits): Q, dO and K are copied to fp16 with one power-of-two
+ *     scale per block of 32 rows or 64 keys, and P and dS enter with scales
+ *     that keep them inside fp16's range. dP = dO V^T of the dQ kernel runs on
+ *     the bf16 inputs.
+ *   S < 512: bf16 products on the inputs, with P and dS entering as hi + lo
+ *     pairs of bf16 values (about 16 significant bits).
  * Returns an attn_status.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

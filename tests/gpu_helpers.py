@@ -65,12 +65,21 @@ def assert_close(name, got, want, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
     assert mn <= mean_abs, f"{name}: mean abs error {mn:.3e} > {mean_abs}"
 
 
-def assert_lse(got, want):
+def assert_lse(got, want, allowance=None):
+    """|err| <= 1e-3 on the fp32 LSE, beyond a per-row allowance when one is given
+    (a bound on how far a stated rounding of the inputs moves the exact LSE)."""
     got = np.asarray(got, dtype=np.float64)
     assert np.all(np.isfinite(got)), "lse: non-finite values"
-    mx, _ = errs(got, want)
-    print(f"    lse: max|err| {mx:.3e}", flush=True)
-    assert mx <= LSE_ABS, f"lse: max abs error {mx:.3e} > {LSE_ABS}"
+    d = np.abs(got - np.asarray(want, dtype=np.float64))
+    mx = float(d.max())
+    if allowance is None:
+        print(f"    lse: max|err| {mx:.3e}", flush=True)
+        assert mx <= LSE_ABS, f"lse: max abs error {mx:.3e} > {LSE_ABS}"
+        return
+    excess = float(np.max(d - allowance))
+    print(f"    lse: max|err| {mx:.3e} (beyond the input-rounding allowance {excess:.3e}; "
+          f"largest allowance {float(np.max(allowance)):.3e})", flush=True)
+    assert excess <= LSE_ABS, f"lse: error beyond the allowance {excess:.3e} > {LSE_ABS}"
 
 
 def run_gpu(x, causal, scale):

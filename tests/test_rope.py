@@ -3,8 +3,12 @@
 Expected values come from oracle.rope: fp64 rotation with the rotated Q and K
 rounded to bf16 (the precision of the attention inputs), the plain attention
 oracle on the rotated pair, gradients rotated back. The same outputs are also
-held against the plain fp64 rotation with no rounding of the rotated pair, at
-the same tolerances: the rounding reading must not hide an error beyond them.
+held against the plain fp64 rotation with no rounding of the rotated pair:
+O, dQ, dK and dV at the same tolerances, and the LSE at 1e-3 beyond the
+amount that rounding the rotated pair to bf16 moves it. That amount has a
+closed bound: the LSE of a row is 1-Lipschitz in the largest change of its
+scores, so it moves by at most max_j |s~_ij - s_ij|, the largest change the
+rounding makes to one of the row's visible scores (computed here exactly).
 """
 import math
 
@@ -52,12 +56,25 @@ def test_rope_against_oracle(case):
     scale = 1.0 / math.sqrt(D)
     g = run(x, causal, scale, base)
     q, k, v, do = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v", "do"))
-    for rounded in (True, False):
-        print(f"  against the oracle with the rotated pair {'rounded to bf16' if rounded else 'in fp64'}")
-        ref = rope.backward(q, k, v, do, scale, causal, base, bf16_rotated=rounded)
+    rnd = rope.backward(q, k, v, do, scale, causal, base, bf16_rotated=True)
+    ext = rope.backward(q, k, v, do, scale, causal, base, bf16_rotated=False)
+    for ref, what in ((rnd, "rounded to bf16"), (ext, "in fp64")):
+        print(f"  against the oracle with the rotated pair {what}")
         for name in ("o", "dq", "dk", "dv"):
             assert_close(name, to_f64(g[name]), ref[name])
-        assert_lse(to_f64(g["lse"]), ref["lse"])
+        allowance = None if ref is rnd else lse_rounding_allowance(rnd, ext, scale, causal, Hq // Hkv)
+        assert_lse(to_f64(g["lse"]), ref["lse"], allowance)
+
+
+def lse_rounding_allowance(rnd, ext, scale, causal, group):
+    """max_j |s~_ij - s_ij| per row: how far rounding the rotated pair moves each score row."""
+    qr, kr = rnd["q_rot"], np.repeat(rnd["k_rot"], group, axis=1)
+    qe, ke = ext["q_rot"], np.repeat(ext["k_rot"], group, axis=1)
+    ds = np.abs(scale * (qr @ np.swapaxes(kr, -1, -2) - qe @ np.swapaxes(ke, -1, -2)))
+    if causal:
+        S = ds.shape[-1]
+        ds = np.where(np.arange(S)[None, :] <= np.arange(S)[:, None], ds, 0.0)
+    return ds.max(axis=-1)
 
 
 def test_rope_at_long_positions_sampled():
@@ -79,13 +96,15 @@ def test_rope_at_long_positions_sampled():
     pos = np.arange(S)
     rows = np.concatenate([np.arange(0, 32), np.arange(S - 64, S), np.random.default_rng(5).choice(S, 32)])
     go, gl = to_f64(o), to_f64(lse)
-    for rounded in (True, False):
-        rnd = rope.round_bf16 if rounded else (lambda a: a)
-        kr = rnd(rope.rotate(kh[0, 0], pos, 1e6))
-        for h in (0, 3):
-            qr = rnd(rope.rotate(qh[0, h][rows], rows, 1e6))
-            s = w.scale * (qr @ kr.T)
-            s = np.where(np.arange(S)[None, :] <= rows[:, None], s, -np.inf)
-            p, l = att.softmax_rows(s)
-            assert_close(f"o rows h{h} ({'bf16' if rounded else 'fp64'} rotation)", go[0, h, rows], p @ vh[0, 0])
-            assert_lse(gl[0, h, rows], l)
+    vis = np.arange(S)[None, :] <= rows[:, None]
+    ke = rope.rotate(kh[0, 0], pos, 1e6)
+    kr = rope.round_bf16(ke)
+    for h in (0, 3):
+        qe = rope.rotate(qh[0, h][rows], rows, 1e6)
+        qr = rope.round_bf16(qe)
+        s_r, s_e = w.scale * (qr @ kr.T), w.scale * (qe @ ke.T)
+        allowance = np.where(vis, np.abs(s_r - s_e), 0.0).max(axis=1)
+        for s, what, allow in ((s_r, "bf16", None), (s_e, "fp64", allowance)):
+            p, l = att.softmax_rows(np.where(vis, s, -np.inf))
+            assert_close(f"o rows h{h} ({what} rotation)", go[0, h, rows], p @ vh[0, 0])
+            assert_lse(gl[0, h, rows], l, allow)
