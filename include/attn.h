@@ -60,7 +60,8 @@ typedef enum attn_status {
     ATTN_ERR_WORKSPACE = 6,              /* workspace missing or smaller than required */
     ATTN_ERR_HIP = 7,                    /* the HIP runtime reported an error at launch */
     ATTN_ERR_BAD_FLAG = 8,               /* causal not 0 or 1 */
-    ATTN_ERR_ALIAS = 9                   /* an output overlaps an input or another output */
+    ATTN_ERR_ALIAS = 9,                  /* an output overlaps an input or another output */
+    ATTN_ERR_SCRATCH_LIMIT = 10          /* attn_bwd_noalloc: sizes need more than its fixed scratch */
 } attn_status;
 
 /*
@@ -144,6 +145,29 @@ int attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
                    void* workspace, size_t workspace_bytes,
                    int B, int Hq, int Hkv, int S, int D, int causal, float scale,
                    hipStream_t stream, hipEvent_t* events);
+
+/*
+ * attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments as attn_bwd minus the workspace,
+ * the same results (the same kernels, bitwise equal outputs) and errors.
+ * The call itself allocates nothing. In place of a caller workspace it uses a
+ * fixed device array inside the library, ATTN_NOALLOC_SCRATCH_BYTES (256 MiB)
+ * on every GPU the library runs on, held from the first use of the library on
+ * that GPU until the process ends. Sizes whose workspace
+ * (attn_bwd_workspace_bytes) exceeds it return ATTN_ERR_SCRATCH_LIMIT and
+ * enqueue nothing; B=1, Hq=64, Hkv=8, S=4096, D=128 needs 202 MiB and fits.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or different host threads, without ordering
+ * between them) race on it and give wrong results. Order them, e.g. on one
+ * stream. The array's contents are not needed between calls (every call
+ * writes what it reads). The current device must be the stream's device.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int S, int D, int causal, float scale,
+                     hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert tam.attn_version() == 1
-    for code in range(10):
+    for code in range(11):
         assert tam.attn_status_string(code) and tam.attn_status_string(code) != "unknown status"
     assert tam.attn_status_string(99) == "unknown status"
 
@@ -235,6 +235,23 @@ def test_block_workspace_covers_every_shorter_key_block(shape):
                                        0, 0, 0.1, None) == 9, sk
         assert lib.attn_bwd_block_dq(A, 2 * A, 3 * A, 4 * A, A + 256, need, B, Hq, Hkv, Sq, sk, D, 1, 0, 0, 0.1,
                                      None) == 9, sk
+
+
+def test_noalloc_rejects_before_touching_the_gpu():
+    """attn_bwd_noalloc validates like attn_bwd, and rejects sizes whose workspace exceeds its
+    fixed scratch (ATTN_ERR_SCRATCH_LIMIT) before looking the scratch up."""
+    lib = tam.load()
+    p = [A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, 8 * A, 9 * A]
+    assert lib.attn_bwd_noalloc(*p, 1, 32, 8, 32768, 128, 1, 0.1, None) == 10
+    assert tam.attn_bwd_workspace_bytes(1, 32, 8, 32768, 128) > tam.NOALLOC_SCRATCH_BYTES
+    assert lib.attn_bwd_noalloc(0, *p[1:], 1, 4, 2, 128, 128, 1, 0.1, None) == 1
+    assert lib.attn_bwd_noalloc(*p, 1, 4, 3, 128, 128, 1, 0.1, None) == 2
+    assert lib.attn_bwd_noalloc(*p, 1, 4, 2, 128, 96, 1, 0.1, None) == 3
+    assert lib.attn_bwd_noalloc(*p, 1, 4, 2, 128, 128, 1, float("inf"), None) == 4
+    assert lib.attn_bwd_noalloc(*p[:6], A + 8, *p[7:], 1, 4, 2, 128, 128, 1, 0.1, None) == 5
+    assert lib.attn_bwd_noalloc(*p, 1, 4, 2, 128, 128, 2, 0.1, None) == 8
+    assert lib.attn_bwd_noalloc(*p[:6], A + 64, *p[7:], 1, 4, 2, 128, 128, 1, 0.1, None) == 9   # dq on q
+    assert lib.attn_bwd_noalloc(*p[:8], 8 * A + 64, 1, 4, 2, 128, 128, 1, 0.1, None) == 9       # dv on dk
 
 
 # ---------------------------------------------------------------------------

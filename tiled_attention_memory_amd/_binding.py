@@ -20,13 +20,15 @@ STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL_POINTER", 2: "ATTN_ERR_BAD_SHAPE",
     3: "ATTN_ERR_UNSUPPORTED_HEAD_DIM", 4: "ATTN_ERR_BAD_SCALE", 5: "ATTN_ERR_MISALIGNED",
     6: "ATTN_ERR_WORKSPACE", 7: "ATTN_ERR_HIP", 8: "ATTN_ERR_BAD_FLAG", 9: "ATTN_ERR_ALIAS",
+    10: "ATTN_ERR_SCRATCH_LIMIT",
 }
 
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_timed", "attn_bwd_workspace_bytes", "attn_status_string",
            "attn_version", "attn_fwd_block", "attn_merge", "attn_bwd_block_workspace_bytes",
            "attn_bwd_block_begin", "attn_bwd_block_dq", "attn_bwd_block_dq_end", "attn_bwd_block_dkdv",
            "attn_decode_workspace_bytes", "attn_decode", "attn_fwd_dropout", "attn_bwd_dropout",
-           "attn_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope")
+           "attn_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope", "attn_bwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 256 << 20
 BWD_EVENTS = 5
 MAX_MERGE = 16
 
@@ -59,6 +61,8 @@ def load() -> ctypes.CDLL:
         lib.attn_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                        i, i, i, i, i, i, f, vp, vp]
         lib.attn_bwd_timed.restype = i
+        lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        lib.attn_bwd_noalloc.restype = i
         lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, ctypes.POINTER(sz)]
         lib.attn_bwd_workspace_bytes.restype = i
         lib.attn_status_string.argtypes = [i]
@@ -84,7 +88,7 @@ def load() -> ctypes.CDLL:
         for name in ("attn_fwd_block", "attn_merge", "attn_bwd_block_workspace_bytes", "attn_bwd_block_begin",
                      "attn_bwd_block_dq", "attn_bwd_block_dq_end", "attn_bwd_block_dkdv",
                      "attn_decode_workspace_bytes", "attn_decode", "attn_fwd_dropout", "attn_bwd_dropout",
-           "attn_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope"):
+                     "attn_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope"):
             getattr(lib, name).restype = i
         _lib = lib
         return lib
@@ -193,6 +197,22 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal=True, scale=No
         st = load().attn_bwd_timed(*args, ctypes.cast(events, ctypes.c_void_p))
     if st != 0:
         raise AttnError(st, "attn_bwd")
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal=True, scale=None, stream=None) -> None:
+    """Enqueue the backward pass without a workspace (the library's fixed scratch):
+    writes dq, dk, dv (bf16) in place. Calls on one GPU must not overlap in time."""
+    import torch
+    B, Hq, Hkv, S, D = _shape(q, k)
+    bf = torch.bfloat16
+    p = [_check(q, "q", bf, (B, Hq, S, D)), _check(k, "k", bf, (B, Hkv, S, D)),
+         _check(v, "v", bf, (B, Hkv, S, D)), _check(o, "o", bf, (B, Hq, S, D)),
+         _check(dout, "dout", bf, (B, Hq, S, D)), _check(lse, "lse", torch.float32, (B, Hq, S)),
+         _check(dq, "dq", bf, (B, Hq, S, D)), _check(dk, "dk", bf, (B, Hkv, S, D)),
+         _check(dv, "dv", bf, (B, Hkv, S, D))]
+    st = load().attn_bwd_noalloc(*p, B, Hq, Hkv, S, D, int(bool(causal)), _scale(scale, D), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_noalloc")
 
 
 # ---------------------------------------------------------------------------

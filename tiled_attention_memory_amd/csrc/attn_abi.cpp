@@ -142,10 +142,12 @@ ATTN_EXPORT int attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, s
 }
 
 namespace {
+// noalloc: no caller workspace; the library's fixed scratch stands in for it
+// (attn_bwd_noalloc), and sizes that need more are rejected.
 int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
                void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D,
                int causal, float scale, int drop_t, unsigned long long seed, hipStream_t stream,
-               hipEvent_t* events) {
+               hipEvent_t* events, bool noalloc = false) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL_POINTER;
   int st = check_common(B, Hq, Hkv, S, S, D, causal, scale);
   if (st != ATTN_OK) return st;
@@ -156,19 +158,26 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   sh.drop_t = drop_t;
   sh.seed = seed;
   const size_t need = tam::bwd_workspace_bytes(sh);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return ATTN_ERR_MISALIGNED;
+  if (noalloc) {
+    if (need > tam::kNoallocScratchBytes) return ATTN_ERR_SCRATCH_LIMIT;
+  } else {
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_MISALIGNED;
+  }
   const size_t qb = (size_t)B * Hq * S * D * 2, kb = (size_t)B * Hkv * S * D * 2;
   const size_t lb = (size_t)B * Hq * S * 4;
   const Range ins[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb), range_of(o, qb),
                        range_of(dout, qb), range_of(lse, lb)};
+  // the scratch is the library's own memory: no caller buffer can overlap it
+  const int n_outs = noalloc ? 3 : 4;
   const Range outs[] = {range_of(dq, qb), range_of(dk, kb), range_of(dv, kb), range_of(workspace, need)};
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < n_outs; ++i) {
     for (const Range& r : ins)
       if (overlap(outs[i], r)) return ATTN_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
+    for (int j = i + 1; j < n_outs; ++j)
       if (overlap(outs[i], outs[j])) return ATTN_ERR_ALIAS;
   }
+  if (noalloc && tam::noalloc_scratch(&workspace) != hipSuccess) return ATTN_ERR_HIP;
   try {
     return from_hip(tam::launch_bwd(sh, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
@@ -206,6 +215,13 @@ ATTN_EXPORT int attn_bwd(const void* q, const void* k, const void* v, const void
                          float scale, hipStream_t stream) {
   return attn_bwd_timed(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, S, D,
                         causal, scale, stream, nullptr);
+}
+
+ATTN_EXPORT int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                 const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S,
+                                 int D, int causal, float scale, hipStream_t stream) {
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, nullptr, 0, B, Hq, Hkv, S, D, causal, scale, 0, 0, stream,
+                    nullptr, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -519,6 +535,9 @@ ATTN_EXPORT const char* attn_status_string(int status) {
     case ATTN_ERR_HIP: return "the HIP runtime reported an error while launching";
     case ATTN_ERR_BAD_FLAG: return "causal must be 0 or 1";
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
+    case ATTN_ERR_SCRATCH_LIMIT:
+      return "these sizes need more backward workspace than the fixed scratch of attn_bwd_noalloc "
+             "(ATTN_NOALLOC_SCRATCH_BYTES); use attn_bwd with a caller workspace";
     default: return "unknown status";
   }
 }

@@ -68,6 +68,12 @@ hipError_t launch_bwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
                       uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t stream,
                       hipEvent_t* events = nullptr);
 
+// Fixed device scratch of attn_bwd_noalloc (one copy per GPU, held until the
+// process ends): its size, and the current device's address of it (looked up
+// on the first call on that device).
+constexpr size_t kNoallocScratchBytes = (size_t)256 << 20;
+hipError_t noalloc_scratch(void** out);
+
 // Block protocol of the backward pass (one query block, key blocks in turn).
 // The need of one block call with sh.Sk keys, and the size that covers every
 // call with a key block of at most sh.Sk keys.
