@@ -63,12 +63,29 @@ def test_dkdv_head_split_follows_balance():
     assert 16 % _head_split(1, 16, 1, 128, 128) == 0
 
 
+def block_call_need(B, Hq, Hkv, Sq, Sk, D):
+    """The workspace one block dK/dV call checks for, found by bisection on its workspace
+    check (dk and dv overlap, an error checked after the workspace, so no call launches)."""
+    import tiled_attention_memory_amd as tam
+    lib = tam.load()
+    A = 1 << 20
+    lo, hi = 0, 1 << 40
+    while lo < hi:
+        m = (lo + hi) // 2
+        st = lib.attn_bwd_block_dkdv(A, 2 * A, 3 * A, 4 * A, 5 * A, 5 * A, 1 << 44, m, B, Hq, Hkv, Sq, Sk, D, 1,
+                                     0, 0, 0.1, None)
+        assert st in (6, 9), st
+        lo, hi = (lo, m) if st == 9 else (m + 1, hi)
+    return lo
+
+
 def test_block_workspace_holds_the_fp16_buffers():
-    """The block protocol's workspace: Delta, lse2 and c (fp32 rows of B*Hq*Sq), the two fp32
+    """The workspace of one block call: Delta, lse2 and c (fp32 rows of B*Hq*Sq), the two fp32
     [B*Hq*Sq, D] sums, the fp16 copies of the query block's Q and dO with three int rows of
     B*Hq*ceil(Sq/32) block exponents, the fp16 copy of a key block's K with two int rows of
     B*Hkv*ceil(Sk/64) tile exponents, each padded to 256 bytes, then nsplit x 2 partial copies of
-    dK/dV when the head subsets number more than one (nsplit divides the group)."""
+    dK/dV when the head subsets number more than one (nsplit divides the group). The size the
+    sizing call returns for the longest key block covers that call too."""
     import tiled_attention_memory_amd as tam
     pad = lambda n: (n + 255) // 256 * 256
     for B, Hq, Hkv, Sq, Sk, D in [(1, 8, 1, 10240, 10240, 128), (1, 64, 8, 512, 512, 128),
@@ -77,9 +94,10 @@ def test_block_workspace_holds_the_fp16_buffers():
         base = (3 * pad(rows * 4) + 2 * pad(rows * D * 4) + 2 * pad(rows * D * 2)
                 + 3 * pad(B * Hq * ((Sq + 31) // 32) * 4)
                 + pad(B * Hkv * Sk * D * 2) + 2 * pad(B * Hkv * ((Sk + 63) // 64) * 4))
-        ws = tam.attn_bwd_block_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
-        assert ws >= base, (ws, base)
+        need = block_call_need(B, Hq, Hkv, Sq, Sk, D)
+        assert need >= base, (need, base)
         part = 2 * B * Hkv * Sk * D * 4
-        assert (ws - base) % part == 0, (ws, base, part)
-        n = max(1, (ws - base) // part)
+        assert (need - base) % part == 0, (need, base, part)
+        n = max(1, (need - base) // part)
         assert (Hq // Hkv) % n == 0, n
+        assert tam.attn_bwd_block_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) >= need
