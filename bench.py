@@ -340,6 +340,99 @@ def decode_bench(args, w):
     print(json.dumps(out), flush=True)
 
 
+def kernel_flops(w):
+    """Algorithmic and executed FLOPs per launch of each kernel of the step.
+
+    Algorithmic: the share of the counted total each kernel carries out -- the
+    forward kernel's two products; the dK/dV kernel's recomputed S and dP plus
+    dV and dK; the dQ kernel's dQ product. Executed adds the dQ kernel's second
+    recomputation of S and dP and its exact-Delta correction product, and, on
+    the bf16 path, the lo halves of the split operands (dV, dK, dQ). The
+    library takes the fp16 path (one product per gradient) for whole-sequence
+    calls over 512 keys or more.
+    """
+    fp16_path = w.S >= 512
+    alg = {
+        "attn_fwd_kernel": w.fwd_flops(),
+        "attn_bwd_dkdv_kernel": 2 * w.fwd_flops(),
+        "attn_bwd_dq_kernel": w.fwd_flops() // 2,
+    }
+    exe = {
+        "attn_fwd_kernel": w.fwd_flops(),
+        "attn_bwd_dkdv_kernel": (2 if fp16_path else 3) * w.fwd_flops(),
+        "attn_bwd_dq_kernel": (4 if fp16_path else 5) * w.fwd_flops() // 2,
+    }
+    return alg, exe
+
+
+def bwd_products(w):
+    """Operand precision of the backward's matrix products for this workload."""
+    if w.S >= 512:
+        return ("fp16 operands with power-of-two block scales (every dK/dV product; S, P K and dQ "
+                "of the dQ kernel), bf16 dP in the dQ kernel; fp32 accumulation")
+    return "bf16 operands, P and dS as hi + lo bf16 pairs; fp32 accumulation"
+
+
+def summarize(w, per, bwd_ms, ms_step, steps_ms, K, warmup, option=None, dropout=0.0, rope=0.0,
+              traffic=measured_traffic):
+    """The bench line from measured times (ms): per-kernel averages `per`, the backward
+    pass `bwd_ms`, the step `ms_step` and the sorted per-step times `steps_ms`."""
+    flops = w.fwd_flops() + w.bwd_flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    alg_flops, exec_flops = kernel_flops(w)
+    if option:
+        # the option entry points take no events between their kernels: report
+        # the forward call and the whole backward call
+        per = {"attn_fwd_kernel": per["attn_fwd_kernel"], "backward_pass": bwd_ms}
+    kernels = {}
+    for name, t in per.items():
+        rec = {"ms": round(t, 4)}
+        if name in alg_flops and t > 0:
+            rec["alg_tflops"] = round(alg_flops[name] / (t * 1e-3) / 1e12, 1)
+            rec["exec_tflops"] = round(exec_flops[name] / (t * 1e-3) / 1e12, 1)
+        kernels[name] = rec
+    dominant = max((n for n in alg_flops if n in per), key=lambda n: per[n])
+    ach = alg_flops[dominant] / (per[dominant] * 1e-3) / 1e12
+    ach_exec = exec_flops[dominant] / (per[dominant] * 1e-3) / 1e12
+    roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if option else traffic(dominant, w.name),
+                # the products the kernel executes, recomputations included
+                "exec_achieved": round(ach_exec, 1), "exec_frac": round(ach_exec / PEAK_BF16_TFLOPS, 4)}
+    fb, bb = alg_bytes(w)
+    return {
+        "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak, causal S=4096 D=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        # inputs and outputs are bf16 (LSE fp32); bwd_products gives the backward's operands
+        "dtype": "bf16",
+        "bwd_products": bwd_products(w),
+        "data": "synthetic",
+        "config": {"workload": w.name + (f"_dropout{dropout:g}" if dropout else "")
+                   + (f"_rope{rope:g}" if rope else ""), "B": w.B,
+                   "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D, "causal": True, "global_batch": w.B,
+                   "seq_len": w.S, "parallelism": "none", **({"dropout": dropout} if dropout else {}),
+                   **({"rope_base": rope} if rope else {})},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "ms_step_median": round(steps_ms[len(steps_ms) // 2], 4),
+        "ms_step_min": round(steps_ms[0], 4),
+        "fwd_tflops": round(w.fwd_flops() / (per["attn_fwd_kernel"] * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),
+        # algorithmic bytes (each tensor once) over the pass time, for the short shapes
+        "fwd_alg_gbps": round(fb / (per["attn_fwd_kernel"] * 1e-3) / 1e9, 1),
+        "bwd_alg_gbps": round(bb / (bwd_ms * 1e-3) / 1e9, 1),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -489,10 +582,6 @@ def main():
         "attn_bwd_reduce_kernel": avg([(e[3], e[4]) for e in ev_b]),
     }
     bwd_ms = avg([(e[0], e[4]) for e in ev_b])
-    if args.dropout or args.rope:
-        # the option entry points take no events between their kernels: report
-        # the forward call and the whole backward call
-        per = {"attn_fwd_kernel": per["attn_fwd_kernel"], "backward_pass": bwd_ms}
     for a, b in ev_f:
         hip.destroy(a)
         hip.destroy(b)
@@ -502,71 +591,12 @@ def main():
 
     # with flushing, the timed region also holds the fills: use the kernels' own events
     ms_step = total_ms / K if flush is None else per["attn_fwd_kernel"] + bwd_ms
-    flops = w.fwd_flops() + w.bwd_flops()
-    value = flops / (ms_step * 1e-3) / 1e12
-    # Algorithmic FLOPs each kernel carries out of the counted total: the forward
-    # kernel's two products; the dK/dV kernel's recomputed S and dP plus dV and dK;
-    # the dQ kernel's dQ. Executed FLOPs add the dQ kernel's second recomputation
-    # of S and dP and its exact-Delta correction product, and, on the bf16 path,
-    # the lo halves of the split operands (dV, dK, dQ). The library takes the fp16
-    # path (one product per gradient) for whole-sequence calls over 512 keys or
-    # more, with or without dropout.
-    fp16_path = w.S >= 512
-    alg_flops = {
-        "attn_fwd_kernel": w.fwd_flops(),
-        "attn_bwd_dkdv_kernel": 2 * w.fwd_flops(),
-        "attn_bwd_dq_kernel": w.fwd_flops() // 2,
-    }
-    exec_flops = {
-        "attn_fwd_kernel": w.fwd_flops(),
-        "attn_bwd_dkdv_kernel": (2 if fp16_path else 3) * w.fwd_flops(),
-        "attn_bwd_dq_kernel": (4 if fp16_path else 5) * w.fwd_flops() // 2,
-    }
-    kernels = {}
-    for name, t in per.items():
-        rec = {"ms": round(t, 4)}
-        if name in alg_flops and t > 0:
-            rec["alg_tflops"] = round(alg_flops[name] / (t * 1e-3) / 1e12, 1)
-            rec["exec_tflops"] = round(exec_flops[name] / (t * 1e-3) / 1e12, 1)
-        kernels[name] = rec
-    dominant = max((n for n in alg_flops if n in per), key=lambda n: per[n])
-    ach = alg_flops[dominant] / (per[dominant] * 1e-3) / 1e12
-    roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": None if (args.dropout or args.rope) else measured_traffic(dominant, w.name)}
+    option = "dropout" if args.dropout else "rope" if args.rope else None
+    out = summarize(w, per, bwd_ms, ms_step, steps_ms, K, args.warmup, option=option, dropout=args.dropout,
+                    rope=args.rope)
+    out["device"] = device_facts(hip)
     log(f"[bench] {K} steps: {ms_step:.4f} ms/step (events), wall {wall / K * 1e3:.4f} ms/step; "
-        f"kernels {kernels}")
-
-    out = {
-        "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak, causal S=4096 D=128",
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": w.name + (f"_dropout{args.dropout:g}" if args.dropout else "")
-                   + (f"_rope{args.rope:g}" if args.rope else ""), "B": w.B,
-                   "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D, "causal": True, "global_batch": w.B,
-                   "seq_len": w.S, "parallelism": "none", **({"dropout": args.dropout} if args.dropout else {}),
-                   **({"rope_base": args.rope} if args.rope else {})},
-        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "ms_step_median": round(steps_ms[K // 2], 4),
-        "ms_step_min": round(steps_ms[0], 4),
-        "fwd_tflops": round(w.fwd_flops() / (per["attn_fwd_kernel"] * 1e-3) / 1e12, 1),
-        "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),
-        # algorithmic bytes (each tensor once) over the pass time, for the short shapes
-        "fwd_alg_gbps": round(alg_bytes(w)[0] / (per["attn_fwd_kernel"] * 1e-3) / 1e9, 1),
-        "bwd_alg_gbps": round(alg_bytes(w)[1] / (bwd_ms * 1e-3) / 1e9, 1),
-        "kernels": kernels,
-        "roofline": roofline,
-        "device": device_facts(hip),
-    }
+        f"kernels {out['kernels']}")
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")

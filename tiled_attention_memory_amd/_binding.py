@@ -14,7 +14,8 @@ import os
 import threading
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libattn.so")
+# TAM_LIBATTN_PATH selects another build of the same library (the tests' host-sanitizer build)
+LIB_PATH = os.environ.get("TAM_LIBATTN_PATH") or os.path.join(_PKG, "lib", "libattn.so")
 
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL_POINTER", 2: "ATTN_ERR_BAD_SHAPE",

@@ -79,6 +79,17 @@ tam::AttnShape square_shape(int B, int Hq, int Hkv, int S, int D, int causal, fl
 
 int from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
+// decode against a key/value cache (attn_decode.h)
+int check_decode(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
+  int st = check_shape(B, Hq, Hkv, Sq, Sk, D);
+  if (st != ATTN_OK) return st;
+  if (Sq > Sk || (long long)(Hq / Hkv) * Sq > 128) return ATTN_ERR_BAD_SHAPE;
+  return ATTN_OK;
+}
+tam::AttnShape decode_shape(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale) {
+  return tam::AttnShape{B, Hq, Hkv, Sq, Sk, D, causal != 0, Sk - Sq, scale};
+}
+
 }  // namespace
 
 extern "C" {
@@ -393,17 +404,6 @@ ATTN_EXPORT int attn_bwd_block_dkdv(const void* q, const void* k, const void* v,
 // ---------------------------------------------------------------------------
 // decode against a key/value cache (attn_decode.h)
 // ---------------------------------------------------------------------------
-namespace {
-int check_decode(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
-  int st = check_shape(B, Hq, Hkv, Sq, Sk, D);
-  if (st != ATTN_OK) return st;
-  if (Sq > Sk || (long long)(Hq / Hkv) * Sq > 128) return ATTN_ERR_BAD_SHAPE;
-  return ATTN_OK;
-}
-tam::AttnShape decode_shape(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale) {
-  return tam::AttnShape{B, Hq, Hkv, Sq, Sk, D, causal != 0, Sk - Sq, scale};
-}
-}  // namespace
 
 ATTN_EXPORT int attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, size_t* bytes) {
   if (!bytes) return ATTN_ERR_NULL_POINTER;
