@@ -57,14 +57,6 @@ struct DecArgs {
 // rescale of the output accumulator.
 constexpr float kLazyMax = 8.f;
 
-// Wait until at most N of this wave's loads are outstanding. Loads return in
-// issue order, so the oldest ones are then complete.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
 // Workgroup barrier without a memory fence: the ring's loads are waited for
 // explicitly (a fence would wait for the loads still in flight as well), and
 // every LDS read before the barrier has been consumed by the time a wave gets

@@ -309,6 +309,14 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // Wait until this wave's outstanding global loads (including loads into LDS) are done.
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N of this wave's vector memory operations are
+// outstanding. They complete in issue order, so the older ones are done.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Dropout on the probabilities, with a keep mask regenerated from a
 // counter-based generator instead of stored: Philox4x32-10 (Salmon, Moraes,
 // Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011).
