@@ -83,6 +83,8 @@ CASES = [
     (1, 8, 1, 333, 128, True, [64, 200], [100]),
     (2, 4, 4, 257, 64, True, [129], [64, 190]),
     (1, 4, 2, 300, 128, False, [111], [150]),
+    # query blocks of 30 and 60 rows: 4 and 2 query heads per unit
+    (1, 8, 2, 90, 128, True, [30], [40]),
     (1, 4, 2, 2200, 128, True, [1000], [1100]),
     (1, 2, 1, 2100, 64, False, [900], [1030]),
 ]

@@ -69,6 +69,9 @@ CASES = [
     (1, 4, 1, 600, 64, True, 0.5),
     (1, 2, 2, 530, 128, False, 0.3),
     (1, 2, 1, 520, 128, True, 0.75),
+    # short sequences: 2 and 4 query heads per unit of the forward and dQ kernels
+    (2, 8, 2, 50, 128, True, 0.2),
+    (1, 8, 2, 24, 64, False, 0.4),
 ]
 
 

@@ -36,6 +36,10 @@ SMALL = [  # B, Hq, Hkv, S, D, causal
     (2, 2, 2, 256, 64, True), (1, 4, 1, 640, 128, True), (1, 2, 2, 1000, 64, True),
     (1, 1, 1, 1, 128, False), (1, 8, 8, 100, 128, False), (1, 4, 2, 257, 64, False),
     (2, 6, 2, 190, 128, False), (1, 2, 1, 520, 128, False),
+    # up to 64 (32) rows, 2 (4) query heads of a group share a unit of the
+    # query-stationary kernels; an odd group keeps one head per unit
+    (2, 8, 2, 20, 128, True), (1, 8, 1, 32, 64, False), (3, 4, 1, 33, 128, True),
+    (1, 6, 2, 17, 64, True), (2, 4, 1, 64, 64, False),
     # 512 keys and more: the fp16 gradient products (ragged, both head sizes, both masks)
     (1, 4, 1, 1100, 128, True), (1, 2, 2, 777, 64, True), (1, 4, 2, 1090, 128, False),
 ]

@@ -44,6 +44,7 @@ CASES = [
     (1, 8, 1, 1000, 128, True, 1e6),
     (2, 4, 4, 129, 64, True, 1e4),
     (1, 6, 2, 190, 128, False, 5e5),
+    (2, 8, 2, 40, 128, True, 1e4),   # 2 query heads per unit
 ]
 
 

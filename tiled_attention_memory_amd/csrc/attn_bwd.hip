@@ -24,7 +24,8 @@
 //             Delta_i = Delta~_i + c_i is written back for kernel 3. This removes
 //             the error that rounding O to bf16 puts into Delta. For the fp16
 //             dK/dV kernel it also writes fp16 copies of Q and dO and the
-//             block exponents of Q, dO and Delta.
+//             block exponents of Q, dO and Delta. Sequences of at most 64 (32)
+//             rows pack 2 (4) query heads of a group into one 128-row unit.
 //   1b. k16:  fp16 copy of K with tile exponents (and those of V), before an
 //             fp16 dQ kernel.
 //   1c. rows16: block protocol only, before an fp16 dK/dV call: the fp16
@@ -954,6 +955,7 @@ struct DqArgs {
   float scale;
   DropParams drop;  // dropout on the probabilities (DROP kernels only)
   const float2* rope_inv;  // (cos, sin) table [Sq][D/2]: rotate dQ back (final mode); null = none
+  int pack;  // log2 of the query heads a unit holds (Sq <= kQBR >> pack)
   TileSched sched;
 };
 
@@ -1006,13 +1008,17 @@ void attn_bwd_dq_kernel(DqArgs a) {
   const bool prole = wave < 4;       // S, P and P K (with Q resident); else dP, dS and dQ (with dO resident)
   const int col = lane & 31, half = lane >> 5;
   const int Sq = a.Sq, Sk = a.Sk, dlt = a.dlt;
+  // unit = (batch, 2^pack query heads of one group, 128-row tile); each head
+  // takes kQBR >> pack rows of it, so a pair's 32 rows belong to one head
+  const int rows_per_head = kQBR >> a.pack;
+  bh = (bh << a.pack) + rblk * 32 / rows_per_head;  // this pair's (batch, query head)
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int kvh = h / (a.Hq / a.Hkv);
   const size_t q_base = (size_t)bh * Sq * D;
   const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)Sk * D;
   const uint16_t* vg = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)Sk * D;
   const int q0 = qt * kQBR;
-  const int wrow0 = q0 + rblk * 32;
+  const int wrow0 = q0 + rblk * 32 % rows_per_head;
   const int qrow = wrow0 + col;
   const uint32_t lds0 = lds_address(smem);
 
@@ -1119,7 +1125,7 @@ void attn_bwd_dq_kernel(DqArgs a) {
   float* const pbuf = reinterpret_cast<float*>(smem + L::PB + rblk * L::PB_BLOCK) + lane;
   auto pb_at = [&](int j) TAM_INLINE { return pbuf + (j & 1) * (L::PB_STAGE / 4); };
 
-  const int last_row = min(q0 + kQBR, Sq) - 1;
+  const int last_row = min(q0 + rows_per_head, Sq) - 1;  // the unit's last row (of any of its heads)
   const int n_kv = (Sk + kQBC - 1) / kQBC;
   // the last key any row of the unit may see is last_row + dlt
   const int ntiles = CAUSAL ? (last_row + dlt < 0 ? 0 : min(n_kv, (last_row + dlt) / kQBC + 1)) : n_kv;
@@ -1611,7 +1617,8 @@ hipError_t launch_dq(const AttnShape& sh, const uint16_t* q, const uint16_t* k, 
   a.scale = sh.scale;
   a.drop = make_drop(sh.drop_t, sh.seed);
   a.rope_inv = sh.rope;
-  a.sched.BH = sh.B * sh.Hq;
+  a.pack = head_pack(sh, kQBR);
+  a.sched.BH = (sh.B * sh.Hq) >> a.pack;
   a.sched.NT = (sh.Sq + kQBR - 1) / kQBR;
   a.sched.chunk = (a.sched.BH + 7) / 8;
   void* args[] = {&a};

@@ -13,7 +13,10 @@
 // this is plain causal attention.
 //
 // Work unit: one (batch, query head, 128-row query tile); 4 waves, each owning
-// 32 query rows. Per 64-key tile:
+// 32 query rows. Sequences of at most 64 (32) rows would leave half (three
+// quarters) of such a unit empty, so there 2 (4) query heads of one group
+// share a unit, each in 64 (32) of its rows: they read the same K and V.
+// Per 64-key tile:
 //   S^T = K Q^T       (MFMA; A = K rows from LDS, B = Q rows held in registers)
 //   online softmax    (each lane owns one query row: its running max, its
 //                      partial row sum and its output column rescale are
@@ -49,6 +52,7 @@ struct FwdArgs {
   float c;  // softmax scale * log2(e): scores are exponentiated in base 2
   DropParams drop;  // dropout on the probabilities (DROP kernels only)
   const float2* rope;  // (cos, sin) table [Sq][D/2]: rotate the Q rows at load; null = none
+  int pack;            // log2 of the query heads a unit holds (Sq <= kBR >> pack)
   TileSched sched;
 };
 
@@ -78,15 +82,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
   const int col = lane & 31, half = lane >> 5;
   const int Sq = a.Sq, Sk = a.Sk, dlt = a.dlt;
-  // unit = (batch, query head, 128-row tile)
+  // unit = (batch, 2^pack query heads of one group, 128-row tile); each head
+  // takes kBR >> pack rows of it, so a wave's 32 rows belong to one head
+  const int rows_per_head = kBR >> a.pack;
+  bh = (bh << a.pack) + wave * 32 / rows_per_head;   // this wave's (batch, query head)
   const int b = bh / a.Hq;
   const int kvh = (bh - b * a.Hq) / (a.Hq / a.Hkv);
-  const int tok = qt * kBR + wave * 32 + col;  // the query row this lane owns
+  const int w_tmin = qt * kBR + wave * 32 % rows_per_head;  // the wave's first row
+  const int w_tmax = w_tmin + 31;
+  const int tok = w_tmin + col;                // the query row this lane owns
   const bool row_ok = tok < Sq;
   const size_t row_off = ((size_t)bh * Sq + tok) * D;  // element offset of the row in q, o (and / D in lse)
-  const int w_tmin = qt * kBR + wave * 32;     // the wave's first row
-  const int w_tmax = w_tmin + 31;
-  const int t_last = min(qt * kBR + kBR, Sq) - 1;
+  const int t_last = min(qt * kBR + rows_per_head, Sq) - 1;  // the unit's last row (of any of its heads)
   constexpr int kbeg = 0;                      // the unit's keys: all of them
   const int kend = Sk;
   const uint16_t* kg = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)Sk * D;
@@ -422,7 +429,8 @@ hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, con
   a.drop = make_drop(sh.drop_t, sh.seed);
   a.rope = sh.rope;
   a.c = sh.scale * kLog2e;
-  a.sched.BH = sh.B * sh.Hq;
+  a.pack = head_pack(sh, kBR);
+  a.sched.BH = (sh.B * sh.Hq) >> a.pack;
   a.sched.NT = (sh.Sq + kBR - 1) / kBR;
   a.sched.chunk = (a.sched.BH + 7) / 8;
   const long long grid = sched_grid(a.sched);

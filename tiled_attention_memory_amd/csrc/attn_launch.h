@@ -26,6 +26,17 @@ struct AttnShape {
   const float2* rope = nullptr;
 };
 
+// Query-stationary kernels give each unit `rows` query rows. A shorter
+// sequence would leave most of a unit empty, so 2^p query heads of one group
+// (which read the same K and V) share it, each in rows >> p of its rows; the
+// packing p (0, 1 or 2) is the largest whose heads still fit.
+inline int head_pack(const AttnShape& sh, int rows) {
+  const int group = sh.Hq / sh.Hkv;
+  if (sh.Sq <= rows / 4 && group % 4 == 0) return 2;
+  if (sh.Sq <= rows / 2 && group % 2 == 0) return 1;
+  return 0;
+}
+
 constexpr int kMaxMerge = 16;  // partial results one merge call combines
 
 // Exactly one of o (bf16) and o32 (fp32) is set.
