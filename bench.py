@@ -340,6 +340,15 @@ def decode_bench(args, w):
     print(json.dumps(out), flush=True)
 
 
+# Whole-sequence calls of at most this many tokens (without dropout or rotation)
+# take the library's one-kernel backward.
+SHORT_MAX = 64
+
+
+def short_path(w, option=None):
+    return w.S <= SHORT_MAX and not option
+
+
 def kernel_flops(w):
     """Algorithmic and executed FLOPs per launch of each kernel of the step.
 
@@ -349,8 +358,13 @@ def kernel_flops(w):
     recomputation of S and dP and its exact-Delta correction product, and, on
     the bf16 path, the lo halves of the split operands (dV, dK, dQ). The
     library takes the fp16 path (one product per gradient) for whole-sequence
-    calls over 512 keys or more.
+    calls over 512 keys or more. Short sequences take one backward kernel that
+    carries the whole counted backward and executes S, dP and the hi and lo
+    halves of dV, dK and dQ.
     """
+    if short_path(w):
+        return ({"attn_fwd_kernel": w.fwd_flops(), "attn_bwd_short_kernel": w.bwd_flops()},
+                {"attn_fwd_kernel": w.fwd_flops(), "attn_bwd_short_kernel": 4 * w.fwd_flops()})
     fp16_path = w.S >= 512
     alg = {
         "attn_fwd_kernel": w.fwd_flops(),
@@ -370,7 +384,8 @@ def bwd_products(w):
     if w.S >= 512:
         return ("fp16 operands with power-of-two block scales (every dK/dV product; S, P K and dQ "
                 "of the dQ kernel), bf16 dP in the dQ kernel; fp32 accumulation")
-    return "bf16 operands, P and dS as hi + lo bf16 pairs; fp32 accumulation"
+    return ("bf16 operands, P and dS as hi + lo bf16 pairs; fp32 accumulation"
+            + (" (one backward kernel)" if short_path(w) else ""))
 
 
 def summarize(w, per, bwd_ms, ms_step, steps_ms, K, warmup, option=None, dropout=0.0, rope=0.0,
@@ -549,14 +564,19 @@ def main():
              if args.flush_mib else None)
     log(f"[bench] {args.warmup} warmup steps done; timing {K} steps")
     # Pass 1, the step time: K steps with events only around the whole run (an
-    # event recorded between two kernels costs about 3 us of stream time).
+    # event recorded between two kernels costs about 3 us of stream time), or,
+    # with flushing, around each step, so that the fills stay outside.
+    ev_s = [(hip.event(), hip.event()) for _ in range(K)] if flush is not None else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     hip.record(e0, sh)
     for i in range(K):
         if flush is not None:
             flush.fill_(float(i))
+            hip.record(ev_s[i][0], sh)
         step()
+        if flush is not None:
+            hip.record(ev_s[i][1], sh)
     hip.record(e1, sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -573,25 +593,37 @@ def main():
         return sum(hip.ms(a, b) for a, b in pairs) / len(pairs)
 
     # per-step times of pass 2, forward start to backward end
-    steps_ms = sorted(hip.ms(ev_f[i][0], ev_b[i][tam.BWD_EVENTS - 1]) for i in range(K))
+    # per-step times, forward start to backward end: pass 1's with flushing, else pass 2's
+    steps_ms = sorted(hip.ms(*ev_s[i]) if flush is not None else hip.ms(ev_f[i][0], ev_b[i][tam.BWD_EVENTS - 1])
+                      for i in range(K))
 
-    per = {
-        "attn_fwd_kernel": avg(ev_f),
-        "attn_bwd_dq_kernel": avg([(e[1], e[2]) for e in ev_b]),
-        "attn_bwd_dkdv_kernel": avg([(e[2], e[3]) for e in ev_b]),
-        "attn_bwd_reduce_kernel": avg([(e[3], e[4]) for e in ev_b]),
-    }
-    bwd_ms = avg([(e[0], e[4]) for e in ev_b])
-    for a, b in ev_f:
-        hip.destroy(a)
-        hip.destroy(b)
+    option = "dropout" if args.dropout else "rope" if args.rope else None
+    if short_path(w, option):
+        # the one-kernel backward lies between events 0 and 1, its partials' sum between 3 and 4
+        per = {
+            "attn_fwd_kernel": avg(ev_f),
+            "attn_bwd_short_kernel": avg([(e[0], e[1]) for e in ev_b]),
+            "attn_bwd_reduce_kernel": avg([(e[3], e[4]) for e in ev_b]),
+        }
+    else:
+        per = {
+            "attn_fwd_kernel": avg(ev_f),
+            "attn_bwd_dq_kernel": avg([(e[1], e[2]) for e in ev_b]),
+            "attn_bwd_dkdv_kernel": avg([(e[2], e[3]) for e in ev_b]),
+            "attn_bwd_reduce_kernel": avg([(e[3], e[4]) for e in ev_b]),
+        }
+    ms_step = total_ms / K if flush is None else avg(ev_s)
+    # The backward's share of the step: the step (pass 1, no events between the
+    # kernels) less the forward kernel. Pass 2's bracket of the backward would
+    # also hold the cost of the events recorded inside it.
+    bwd_ms = ms_step - per["attn_fwd_kernel"]
+    for pair in ev_f + (ev_s or []):
+        for e in pair:
+            hip.destroy(e)
     for e in ev_b:
         for j in range(tam.BWD_EVENTS):
             hip.destroy(e[j])
 
-    # with flushing, the timed region also holds the fills: use the kernels' own events
-    ms_step = total_ms / K if flush is None else per["attn_fwd_kernel"] + bwd_ms
-    option = "dropout" if args.dropout else "rope" if args.rope else None
     out = summarize(w, per, bwd_ms, ms_step, steps_ms, K, args.warmup, option=option, dropout=args.dropout,
                     rope=args.rope)
     out["device"] = device_facts(hip)

@@ -84,9 +84,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * LSE in base 2 (fp32); fp16 copies of Q, dO and K scaled by powers of two,
  * with one exponent per 32-row block of Q and dO (and of Delta) and per
  * 64-key tile of K and V; and, when the query heads of a group are split into
- * subsets for load balance, fp32 dK/dV partials of each subset. Examples:
- * B=1, Hq=64, Hkv=8, S=4096, D=128 needs 202 MiB; B=1, Hq=8, Hkv=1, S=81920,
- * D=128 needs 665 MiB.
+ * subsets for load balance, fp32 dK/dV partials of each subset (the
+ * one-kernel pass of S <= 64 uses only its partials). Examples: B=1, Hq=64,
+ * Hkv=8, S=4096, D=128 needs 202 MiB; B=1, Hq=8, Hkv=1, S=81920, D=128 needs
+ * 665 MiB.
  * Returns ATTN_OK, ATTN_ERR_NULL_POINTER (bytes NULL), ATTN_ERR_BAD_SHAPE or
  * ATTN_ERR_UNSUPPORTED_HEAD_DIM.
  */
@@ -107,7 +108,9 @@ int attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes
  *                      and on return are unspecified.
  * dK and dV are accumulated without atomics; the results are bitwise
  * reproducible for the same inputs and sizes. The row term Delta is made
- * exact inside the pass (not taken from the rounded o alone).
+ * exact inside the pass (not taken from the rounded o alone). For S <= 64
+ * every row's keys fit one tile and a single kernel forms dQ, dK and dV,
+ * with Delta = sum_j P_ij dP_ij over the whole row (o is then not read).
  * Precision of the matrix products (every one accumulates in fp32; the
  * outputs are rounded to bf16 once, at the end):
  *   S >= 512: every product of the dK/dV kernel (S, dP, dV, dK) and the dQ
@@ -116,8 +119,9 @@ int attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, size_t* bytes
  *     scale per block of 32 rows or 64 keys, and P and dS enter with scales
  *     that keep them inside fp16's range. dP = dO V^T of the dQ kernel runs on
  *     the bf16 inputs.
- *   S < 512: bf16 products on the inputs, with P and dS entering as hi + lo
- *     pairs of bf16 values (about 16 significant bits).
+ *   S < 512 (and the one-kernel pass of S <= 64): bf16 products on the
+ *     inputs, with P and dS entering as hi + lo pairs of bf16 values (about
+ *     16 significant bits).
  * Returns an attn_status.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -130,11 +134,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * attn_bwd for measurement tools: identical arguments, results and errors,
  * plus ATTN_BWD_EVENTS caller-created events (hipEventCreate) recorded on
  * `stream` around the backward kernels:
- *   events[0], events[1] before the dQ kernel, back to back (the row terms,
- *             Delta from the stored O and the scaled LSE, are formed inside
- *             the dQ kernel; the slot is kept so the layout stays the same)
- *   events[2] after the dQ kernel, before the dK/dV kernel
- *   events[3] after the dK/dV kernel
+ *   events[0] first
+ *   events[1] after the fp16 copy of K (S >= 512; else right after events[0]),
+ *             before the dQ kernel; for S <= 64, after the one-kernel pass
+ *   events[2] after the dQ kernel, before the dK/dV kernel (S <= 64: right
+ *             after events[1])
+ *   events[3] after the dK/dV kernel (S <= 64: right after events[2])
  *   events[4] after the fixed-order sum of per-head-subset dK/dV partials
  *             (recorded right after events[3] when no partials are used)
  * The events stay owned by the caller; pass NULL to behave exactly like attn_bwd.

@@ -98,6 +98,21 @@ def test_short_sequences_report_the_bf16_products():
     assert "hi + lo" in bench.bwd_products(wl.BY_NAME["llama3_405b_lora_b16_s64"])
 
 
+def test_short_sequences_take_the_one_kernel_backward():
+    """Up to 64 tokens the backward is one kernel: it carries the whole counted backward
+    and executes S, dP and both halves of dV, dK and dQ (8 products of fwd/2 each)."""
+    w = wl.BY_NAME["llama3_405b_lora_b16_s64"]
+    alg, exe = bench.kernel_flops(w)
+    assert set(alg) == {"attn_fwd_kernel", "attn_bwd_short_kernel"}
+    assert alg["attn_bwd_short_kernel"] == w.bwd_flops() and exe["attn_bwd_short_kernel"] == 4 * w.fwd_flops()
+    assert "one backward kernel" in bench.bwd_products(w)
+    assert not bench.short_path(w, option="dropout")
+    per = {"attn_fwd_kernel": 0.02, "attn_bwd_short_kernel": 0.03, "attn_bwd_reduce_kernel": 0.005}
+    out = bench.summarize(w, per, 0.04, 0.06, [0.06], K=1, warmup=0, traffic=lambda kernel, workload: None)
+    assert out["roofline"]["kernel"] == "attn_bwd_short_kernel"
+    assert out["bwd_alg_gbps"] == round(bench.alg_bytes(w)[1] / 0.04e-3 / 1e9, 1)
+
+
 def test_cpu_baseline_record():
     w = wl.WORKLOADS[0]
     x = wl.workload_inputs(w)

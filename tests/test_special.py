@@ -46,9 +46,10 @@ def test_equal_weights_give_running_mean(D, mode):
     assert_lse(to_f64(gpu["lse"]), np.broadcast_to(np.log(np.arange(1, S + 1)), (B, Hq, S)))
 
 
-@pytest.mark.parametrize("S", [257, 600])
+@pytest.mark.parametrize("S", [48, 257, 600])
 def test_zero_output_gradient_gives_zero_gradients(S):
-    # S = 600: the fp16 gradient products, with an all-zero dO in every block
+    # S = 48: the one-kernel backward of short sequences; S = 600: the fp16
+    # gradient products, with an all-zero dO in every block
     say(f"dO = 0, S = {S}")
     x = wl.make_inputs(1, 8, 2, S, 128, seed=(202,))
     x["do"] = np.zeros_like(x["do"])
@@ -57,10 +58,13 @@ def test_zero_output_gradient_gives_zero_gradients(S):
         assert np.all(to_f64(gpu[name]) == 0.0), name
 
 
-@pytest.mark.parametrize("scale,k_mult,causal", [(-0.2, 1.0, True), (0.5, 3.0, True), (-0.3, 2.0, False)])
-def test_unusual_scales_against_oracle(scale, k_mult, causal):
-    say(f"scale={scale} k_mult={k_mult} causal={causal}")
-    B, Hq, Hkv, S, D = 1, 4, 2, 200, 128
+@pytest.mark.parametrize("scale,k_mult,causal,S", [
+    (-0.2, 1.0, True, 200), (0.5, 3.0, True, 200), (-0.3, 2.0, False, 200),
+    # the one-kernel backward of short sequences
+    (0.5, 3.0, True, 64), (-0.3, 2.0, False, 40)])
+def test_unusual_scales_against_oracle(scale, k_mult, causal, S):
+    say(f"scale={scale} k_mult={k_mult} causal={causal} S={S}")
+    B, Hq, Hkv, D = 1, 4, 2, 128
     x = wl.make_inputs(B, Hq, Hkv, S, D, seed=(203, int(1000 * abs(scale)), int(scale < 0), int(causal)), k_mult=k_mult)
     gpu = run_gpu(x, causal, scale)
     q, k, v, do = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v", "do"))

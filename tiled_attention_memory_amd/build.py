@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libattn.so")
 SOURCES = ["attn_abi.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_merge.hip", "attn_rope.hip",
-           "attn_decode.hip", "attn_noalloc.hip"]
+           "attn_decode.hip", "attn_noalloc.hip", "attn_bwd_short.hip"]
 
 
 def hipcc() -> str:

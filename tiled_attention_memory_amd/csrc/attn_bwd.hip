@@ -196,6 +196,14 @@ WsLayout ws_layout(const AttnShape& sh, bool block = false) {
   w.part = off;
   const size_t kv_elems = (size_t)sh.B * sh.Hkv * sh.Sk * sh.D;
   w.total = w.part + (w.nsplit > 1 ? align256((size_t)w.nsplit * 2 * kv_elems * 4) : 0);
+  // a whole-sequence call of at most 64 tokens may take the one-kernel path,
+  // whose only workspace is its partials (from offset 0)
+  if (!block) {
+    AttnShape s = sh;
+    s.drop_t = 0;
+    s.rope = nullptr;
+    if (bwd_short_path(s)) w.total = std::max(w.total, align256(bwd_short_workspace_bytes(s)));
+  }
   return w;
 }
 
@@ -1697,14 +1705,7 @@ hipError_t launch_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k
 }
 
 hipError_t launch_reduce(const AttnShape& sh, uint16_t* dk, uint16_t* dv, const Ws& ws, hipStream_t stream) {
-  if (ws.w.nsplit <= 1) return hipSuccess;
-  const long long n4 = (long long)sh.B * sh.Hkv * sh.Sk * sh.D / 4;
-  const long long grid = (n4 + kThreads - 1) / kThreads;
-  int ns = ws.w.nsplit;
-  float* part = ws.part;
-  void* args[] = {(void*)&part, (void*)&dk, (void*)&dv, (void*)&n4, (void*)&ns};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_reduce_kernel), dim3((unsigned)grid),
-                         dim3(kThreads), args, 0, stream);
+  return launch_bwd_reduce(sh, ws.part, ws.w.nsplit, dk, dv, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -1712,9 +1713,19 @@ hipError_t launch_all(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
                       const uint16_t* o, const uint16_t* dout, const float* lse, uint16_t* dq,
                       uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t stream,
                       hipEvent_t* ev) {
-  const Ws ws(sh, workspace, false);
   hipError_t e;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  if (bwd_short_path(sh)) {
+    // one kernel (between marks 0 and 1), then the sum of its partials (3 to 4)
+    float* part = static_cast<float*>(workspace);
+    if ((e = mark(0)) != hipSuccess ||
+        (e = launch_bwd_short(sh, q, k, v, dout, lse, dq, dk, dv, part, stream)) != hipSuccess ||
+        (e = mark(1)) != hipSuccess || (e = mark(2)) != hipSuccess || (e = mark(3)) != hipSuccess ||
+        (e = launch_bwd_reduce(sh, part, bwd_short_split(sh), dk, dv, stream)) != hipSuccess)
+      return e;
+    return mark(4);
+  }
+  const Ws ws(sh, workspace, false);
   if ((e = mark(0)) != hipSuccess) return e;
   // 1. the fp16 copy of K for the fp16 dQ kernel (Delta~ and lse2 are formed
   //    inside the dQ kernel on this path)
@@ -1774,6 +1785,16 @@ hipError_t block_dkdv(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
 }
 
 }  // namespace
+
+hipError_t launch_bwd_reduce(const AttnShape& sh, const float* part, int ns, uint16_t* dk, uint16_t* dv,
+                             hipStream_t stream) {
+  if (ns <= 1) return hipSuccess;
+  long long n4 = (long long)sh.B * sh.Hkv * sh.Sk * sh.D / 4;
+  const long long grid = (n4 + kThreads - 1) / kThreads;
+  void* args[] = {(void*)&part, (void*)&dk, (void*)&dv, (void*)&n4, (void*)&ns};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_reduce_kernel), dim3((unsigned)grid),
+                         dim3(kThreads), args, 0, stream);
+}
 
 size_t bwd_workspace_bytes(const AttnShape& sh) { return ws_layout(sh).total; }
 size_t bwd_block_workspace_bytes(const AttnShape& sh) { return ws_layout(sh, true).total; }

@@ -317,6 +317,16 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier that orders LDS accesses only: every LDS access of this
+// wave before it is complete and none after it starts early, but loads from
+// global memory that are still in flight (into LDS stages nobody reads yet)
+// are not waited for, as a full barrier would.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Dropout on the probabilities, with a keep mask regenerated from a
 // counter-based generator instead of stored: Philox4x32-10 (Salmon, Moraes,
 // Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011).

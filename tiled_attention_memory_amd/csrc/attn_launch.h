@@ -79,6 +79,19 @@ hipError_t launch_bwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k,
                       uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t stream,
                       hipEvent_t* events = nullptr);
 
+// Whole-sequence backward of at most 64 tokens (no dropout, no rotation): one
+// kernel forms dQ, dK and dV; with several head subsets it leaves fp32 dK/dV
+// partials ([nsplit][2][B*Hkv*S*D] at `part`) for the fixed-order reduce.
+bool bwd_short_path(const AttnShape& sh);
+int bwd_short_split(const AttnShape& sh);
+size_t bwd_short_workspace_bytes(const AttnShape& sh);
+hipError_t launch_bwd_short(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const uint16_t* dout, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                            float* part, hipStream_t stream);
+// Fixed-order sum of ns fp32 partials [ns][2][B*Hkv*Sk*D] into bf16 dK, dV.
+hipError_t launch_bwd_reduce(const AttnShape& sh, const float* part, int ns, uint16_t* dk, uint16_t* dv,
+                             hipStream_t stream);
+
 // Fixed device scratch of attn_bwd_noalloc (one copy per GPU, held until the
 // process ends): its size, and the current device's address of it (looked up
 // on the first call on that device).
