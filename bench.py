@@ -473,9 +473,9 @@ def main():
                          "memory-side cache start cold (for the short, bandwidth-bound shapes); "
                          "the step time is then the sum of the per-kernel event times")
     ap.add_argument("--flush-mode", choices=("read", "write"), default="read",
-                    help="with --decode and --flush-mib: evict the cache by reading the buffer "
-                         "(default) or by overwriting it, which leaves dirty lines whose write-back "
-                         "overlaps the timed call")
+                    help="with --flush-mib: evict the cache by reading the buffer (default) or by "
+                         "overwriting it, which leaves dirty lines whose write-back overlaps the "
+                         "timed call")
     ap.add_argument("--cpu-groups", type=int, default=8)
     ap.add_argument("--hbm-probe", type=int, default=0, metavar="MIB",
                     help="instead of attention: achievable HBM bandwidth of plain library kernels "
@@ -570,9 +570,19 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     hip.record(e0, sh)
+    def evict(i):
+        # reading evicts the cache without leaving dirty lines whose write-back
+        # would compete with the timed step; --flush-mode write measures that case
+        if args.flush_mode == "write":
+            flush.fill_(float(i))
+        else:
+            flush.sum()
+
+    if flush is not None:
+        flush.fill_(1.0)
     for i in range(K):
         if flush is not None:
-            flush.fill_(float(i))
+            evict(i)
             hip.record(ev_s[i][0], sh)
         step()
         if flush is not None:
@@ -585,7 +595,7 @@ def main():
     log(f"[bench] timing {K} more steps with per-kernel events")
     for i in range(K):
         if flush is not None:
-            flush.fill_(float(i))
+            evict(i)
         step(ev_f[i], ev_b[i])
     torch.cuda.synchronize()
 
@@ -626,6 +636,8 @@ def main():
 
     out = summarize(w, per, bwd_ms, ms_step, steps_ms, K, args.warmup, option=option, dropout=args.dropout,
                     rope=args.rope)
+    out["config"]["cache"] = ("warm" if flush is None else "cold" if args.flush_mode == "read"
+                              else "cold, after a write")
     out["device"] = device_facts(hip)
     log(f"[bench] {K} steps: {ms_step:.4f} ms/step (events), wall {wall / K * 1e3:.4f} ms/step; "
         f"kernels {out['kernels']}")

@@ -96,7 +96,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_short_kernel(ShortArgs a
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
 
   const int S = a.S;
-  const int grp = blockIdx.x / a.nsplit, sub = blockIdx.x - grp * a.nsplit;  // grp = b * Hkv + kv head
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);  // the subsets of a kv head share an XCD
+  const int grp = unit / a.nsplit, sub = unit - grp * a.nsplit;  // grp = b * Hkv + kv head
   const int b = grp / a.Hkv, kvh = grp - b * a.Hkv;
   const int hps = a.Hq / a.Hkv / a.nsplit;          // query heads per subset
   const int h_first = kvh * (a.Hq / a.Hkv) + sub * hps;

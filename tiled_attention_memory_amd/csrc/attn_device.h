@@ -445,6 +445,14 @@ __host__ __device__ inline long long sched_grid(const TileSched& s) {
   return s.BH % 8 == 0 ? 8LL * s.chunk * s.NT : (long long)s.BH * s.NT;
 }
 
+// Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i % 8). For
+// a grid that is a multiple of 8, unit = xcd_unit(i, n) gives each XCD a
+// contiguous range of units, so that neighbouring units (which share inputs)
+// share that XCD's L2.
+__device__ __forceinline__ int xcd_unit(int bid, int n) {
+  return n % 8 == 0 ? (bid & 7) * (n >> 3) + (bid >> 3) : bid;
+}
+
 __host__ __device__ inline bool sched_decode(const TileSched& s, int bid, int* bh, int* qt) {
   if (s.BH % 8 != 0) {
     if (bid >= s.BH * s.NT) return false;

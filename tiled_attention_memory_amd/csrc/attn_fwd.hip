@@ -411,6 +411,159 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// Whole sequences of at most 64 tokens: every row's keys fit one 64-key tile,
+// so the softmax needs no running max and K, V can serve many query heads.
+// Unit: (batch, kv head, subset of the group's query heads), 4 waves. K and V
+// go to LDS once; waves 2p and 2p + 1 take rows 0..31 and 32..63 of the
+// subset's heads p, p + 2, ..., each holding its rows of Q in registers while
+// the next head's rows load. With no barrier after the first, the waves run
+// independently.
+struct FwdShortArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int Hq, Hkv, S, nsplit;
+  float c;  // softmax scale * log2(e)
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_short_kernel(FwdShortArgs a) {
+  using T = SwzTile<D>;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int NLD = T::LOADS / 4;
+  static_assert(kBC == T::ROWS, "key tile = LDS tile");
+  __shared__ __attribute__((aligned(1024))) unsigned char kv[2 * T::BYTES];  // K tile, then V tile
+
+  const int S = a.S;
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  const int grp = unit / a.nsplit, sub = unit - grp * a.nsplit;  // grp = b * Hkv + kv head
+  const int b = grp / a.Hkv;
+  const int g = a.Hq / a.Hkv, hps = g / a.nsplit;
+  const int h_end = (grp - b * a.Hkv) * g + sub * hps + hps;     // past the subset's last head
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int rb = wave & 1;                 // this wave's 32 rows of each head
+  const int tok = 32 * rb + col;           // the query row this lane owns
+  const bool row_ok = tok < S;
+  const float c = fabsf(a.c);
+  const uint32_t flip = a.c < 0.f ? 0x80008000u : 0u;  // a negative scale is folded into Q
+
+  {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (size_t)grp * S * D, S * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (size_t)grp * S * D, S * D * 2);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int li = wave * NLD + i;
+      load_lds16(rk, kv + li * 1024, T::load_src(li, lane));
+      load_lds16(rv, kv + T::BYTES + li * 1024, T::load_src(li, lane));
+    }
+  }
+  auto load_q = [&](int h, u32x4 (&w)[KS]) TAM_INLINE {
+    const uint16_t* qp = a.q + (((size_t)b * a.Hq + h) * S + tok) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) w[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+  };
+  int h = h_end - hps + (wave >> 1);
+  u32x4 qn[KS];
+  if (h < h_end) load_q(h, qn);
+  wait_loads();
+  __syncthreads();
+
+  int koff[KS], voff[DB][2];
+  const int i16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = T::chunk_off(col, 2 * ks + half);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+      voff[db][hi] = T::elem_off(4 * half + (i16 >> 2) + 8 * hi, db * 32 + dsub + 4 * (i16 & 3));
+  // the last key row tok may see, less this lane's key offset 4 half
+  const int lim = (CAUSAL ? min(tok, S - 1) : S - 1) - 4 * half;
+  auto visible = [&](int kb, int v) TAM_INLINE { return kb * 32 + 8 * (v >> 2) + (v & 3) <= lim; };
+
+  // one head: S^T for key blocks 0 .. NKB - 1, softmax over the row, O^T = V^T P^T
+  auto head = [&](auto nkb_tag, const bf16x8 (&qf)[KS], int hh) TAM_INLINE {
+    constexpr int NKB = decltype(nkb_tag)::value;
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kv + kb * 32 * T::ROW_BYTES + koff[ks]), qf[ks], s[kb]);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = visible(kb, v) ? fmaxf(mx, s[kb][v]) : mx;
+    const float mt = max_halves(mx) * c;  // every row sees key 0: finite
+    float p[NKB][16];
+    float l = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        p[kb][v] = visible(kb, v) ? fast_exp2(fmaf(s[kb][v], c, -mt)) : 0.f;
+        l += p[kb][v];
+      }
+    l = sum_halves(l);
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const bf16x8 pb = pack_bf16x8(&p[kb][8 * k2]);
+        const unsigned char* vp = kv + T::BYTES + (kb * 32 + k2 * 16) * T::ROW_BYTES;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc[db] = mfma32(lds_read_tr_pair(reinterpret_cast<const uint16_t*>(vp + voff[db][0]),
+                                            reinterpret_cast<const uint16_t*>(vp + voff[db][1])),
+                           pb, acc[db]);
+      }
+    if (row_ok) {
+      const float inv = 1.f / l;
+      const size_t row = ((size_t)b * a.Hq + hh) * S + tok;
+      uint16_t* op = a.o + row * D + 8 * half;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          u32x2 w[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int i = 2 * m + t;
+            w[t] = u32x2{pack_bf16(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv),
+                         pack_bf16(acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv)};
+          }
+          *reinterpret_cast<u32x4*>(op + 32 * db + 16 * m) = pair_halves(w[0], w[1]);
+        }
+      if (half == 0) a.lse[row] = (mt + __log2f(l)) * kLn2;
+    }
+  };
+
+  // rows 0..31 see only keys 0..31 under a causal mask, and so does every row of S <= 32
+  const bool one_block = (CAUSAL && rb == 0) || S <= 32;
+  for (; h < h_end; h += 2) {
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qn[ks] ^ flip);
+    if (h + 2 < h_end) load_q(h + 2, qn);  // the next head's rows load meanwhile
+    if (one_block)
+      head(std::integral_constant<int, 1>{}, qf, h);
+    else
+      head(std::integral_constant<int, 2>{}, qf, h);
+  }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   uint16_t* o, float* o32, float* lse, hipStream_t stream) {
@@ -440,10 +593,47 @@ hipError_t launch(const AttnShape& sh, const uint16_t* q, const uint16_t* k, con
   return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
 }
 
+// The fewest head subsets (a divisor of the group) that give every compute
+// unit two workgroups.
+int fwd_short_split(const AttnShape& sh) {
+  const int g = sh.Hq / sh.Hkv;
+  const long long groups = (long long)sh.B * sh.Hkv;
+  for (int ns = 1; ns < g; ++ns)
+    if (g % ns == 0 && groups * ns >= 512) return ns;
+  return g;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_short(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        uint16_t* o, float* lse, hipStream_t stream) {
+  FwdShortArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.Hq = sh.Hq;
+  a.Hkv = sh.Hkv;
+  a.S = sh.Sq;
+  a.nsplit = fwd_short_split(sh);
+  a.c = sh.scale * kLog2e;
+  const long long grid = (long long)sh.B * sh.Hkv * a.nsplit;
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_short_kernel<D, CAUSAL>), dim3((unsigned)grid),
+                         dim3(kThreads), args, 0, stream);
+}
+
 }  // namespace
 
 hipError_t launch_fwd(const AttnShape& sh, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       uint16_t* o, float* o32, float* lse, hipStream_t stream) {
+  // whole sequences of at most one key tile, bf16 output, no dropout or rotation
+  if (o && !o32 && sh.Sq == sh.Sk && sh.Sq <= kBC && sh.dlt == 0 && !sh.drop_t && !sh.rope) {
+    if (sh.D == 128) return sh.causal ? launch_short<128, true>(sh, q, k, v, o, lse, stream)
+                                      : launch_short<128, false>(sh, q, k, v, o, lse, stream);
+    return sh.causal ? launch_short<64, true>(sh, q, k, v, o, lse, stream)
+                     : launch_short<64, false>(sh, q, k, v, o, lse, stream);
+  }
   if (sh.D == 128) return sh.causal ? launch<128, true>(sh, q, k, v, o, o32, lse, stream)
                                     : launch<128, false>(sh, q, k, v, o, o32, lse, stream);
   return sh.causal ? launch<64, true>(sh, q, k, v, o, o32, lse, stream)
