@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 bf16 flop/clk x 2.4 GHz (AMD's 2.5 PFLOP/s dense figure)
 PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.json")
-KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
+KERNEL_SOURCES = ["attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_short.hip"]
 
 
 def log(msg):
@@ -363,8 +363,8 @@ def kernel_flops(w):
     halves of dV, dK and dQ.
     """
     if short_path(w):
-        return ({"attn_fwd_kernel": w.fwd_flops(), "attn_bwd_short_kernel": w.bwd_flops()},
-                {"attn_fwd_kernel": w.fwd_flops(), "attn_bwd_short_kernel": 4 * w.fwd_flops()})
+        return ({"attn_fwd_short_kernel": w.fwd_flops(), "attn_bwd_short_kernel": w.bwd_flops()},
+                {"attn_fwd_short_kernel": w.fwd_flops(), "attn_bwd_short_kernel": 4 * w.fwd_flops()})
     fp16_path = w.S >= 512
     alg = {
         "attn_fwd_kernel": w.fwd_flops(),
@@ -377,6 +377,17 @@ def kernel_flops(w):
         "attn_bwd_dq_kernel": (4 if fp16_path else 5) * w.fwd_flops() // 2,
     }
     return alg, exe
+
+
+def short_kernel_bytes(w):
+    """Algorithmic bytes of the one-kernel paths, each tensor they must touch once: the
+    forward reads Q, K, V and writes O, LSE; the backward reads Q, K, V, dO, LSE and
+    writes dQ, dK, dV (it needs neither O nor a Delta round trip)."""
+    q = w.B * w.Hq * w.S * w.D * 2
+    kv = w.B * w.Hkv * w.S * w.D * 2
+    rows = w.B * w.Hq * w.S * 4
+    return {"attn_fwd_short_kernel": 2 * q + 2 * kv + rows,
+            "attn_bwd_short_kernel": 3 * q + 4 * kv + rows}
 
 
 def bwd_products(w):
@@ -395,10 +406,13 @@ def summarize(w, per, bwd_ms, ms_step, steps_ms, K, warmup, option=None, dropout
     flops = w.fwd_flops() + w.bwd_flops()
     value = flops / (ms_step * 1e-3) / 1e12
     alg_flops, exec_flops = kernel_flops(w)
+    fwd_ms = per["attn_fwd_kernel"]
     if option:
         # the option entry points take no events between their kernels: report
         # the forward call and the whole backward call
-        per = {"attn_fwd_kernel": per["attn_fwd_kernel"], "backward_pass": bwd_ms}
+        per = {"attn_fwd_kernel": fwd_ms, "backward_pass": bwd_ms}
+    elif short_path(w):
+        per = {("attn_fwd_short_kernel" if n == "attn_fwd_kernel" else n): t for n, t in per.items()}
     kernels = {}
     for name, t in per.items():
         rec = {"ms": round(t, 4)}
@@ -407,13 +421,19 @@ def summarize(w, per, bwd_ms, ms_step, steps_ms, K, warmup, option=None, dropout
             rec["exec_tflops"] = round(exec_flops[name] / (t * 1e-3) / 1e12, 1)
         kernels[name] = rec
     dominant = max((n for n in alg_flops if n in per), key=lambda n: per[n])
-    ach = alg_flops[dominant] / (per[dominant] * 1e-3) / 1e12
-    ach_exec = exec_flops[dominant] / (per[dominant] * 1e-3) / 1e12
-    roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": None if option else traffic(dominant, w.name),
-                # the products the kernel executes, recomputations included
-                "exec_achieved": round(ach_exec, 1), "exec_frac": round(ach_exec / PEAK_BF16_TFLOPS, 4)}
+    if short_path(w, option):
+        # one key tile per row: a few products per byte, so the bound is HBM
+        ach = short_kernel_bytes(w)[dominant] / (per[dominant] * 1e-3) / 1e9
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic(dominant, w.name)}
+    else:
+        ach = alg_flops[dominant] / (per[dominant] * 1e-3) / 1e12
+        ach_exec = exec_flops[dominant] / (per[dominant] * 1e-3) / 1e12
+        roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 1),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None if option else traffic(dominant, w.name),
+                    # the products the kernel executes, recomputations included
+                    "exec_achieved": round(ach_exec, 1), "exec_frac": round(ach_exec / PEAK_BF16_TFLOPS, 4)}
     fb, bb = alg_bytes(w)
     return {
         "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak, causal S=4096 D=128",
@@ -438,10 +458,10 @@ def summarize(w, per, bwd_ms, ms_step, steps_ms, K, warmup, option=None, dropout
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "ms_step_median": round(steps_ms[len(steps_ms) // 2], 4),
         "ms_step_min": round(steps_ms[0], 4),
-        "fwd_tflops": round(w.fwd_flops() / (per["attn_fwd_kernel"] * 1e-3) / 1e12, 1),
+        "fwd_tflops": round(w.fwd_flops() / (fwd_ms * 1e-3) / 1e12, 1),
         "bwd_tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),
         # algorithmic bytes (each tensor once) over the pass time, for the short shapes
-        "fwd_alg_gbps": round(fb / (per["attn_fwd_kernel"] * 1e-3) / 1e9, 1),
+        "fwd_alg_gbps": round(fb / (fwd_ms * 1e-3) / 1e9, 1),
         "bwd_alg_gbps": round(bb / (bwd_ms * 1e-3) / 1e9, 1),
         "kernels": kernels,
         "roofline": roofline,

@@ -103,14 +103,23 @@ def test_short_sequences_take_the_one_kernel_backward():
     and executes S, dP and both halves of dV, dK and dQ (8 products of fwd/2 each)."""
     w = wl.BY_NAME["llama3_405b_lora_b16_s64"]
     alg, exe = bench.kernel_flops(w)
-    assert set(alg) == {"attn_fwd_kernel", "attn_bwd_short_kernel"}
+    assert set(alg) == {"attn_fwd_short_kernel", "attn_bwd_short_kernel"}
     assert alg["attn_bwd_short_kernel"] == w.bwd_flops() and exe["attn_bwd_short_kernel"] == 4 * w.fwd_flops()
     assert "one backward kernel" in bench.bwd_products(w)
     assert not bench.short_path(w, option="dropout")
+    # bytes each one-kernel pass must touch (MB = 1e6): fwd Q, K, V in, O, LSE out;
+    # bwd Q, K, V, dO, LSE in, dQ, dK, dV out
+    b = bench.short_kernel_bytes(w)
+    assert round(b["attn_fwd_short_kernel"] / 1e6, 1) == 71.8 and round(b["attn_bwd_short_kernel"] / 1e6, 1) == 109.6
     per = {"attn_fwd_kernel": 0.02, "attn_bwd_short_kernel": 0.03, "attn_bwd_reduce_kernel": 0.005}
-    out = bench.summarize(w, per, 0.04, 0.06, [0.06], K=1, warmup=0, traffic=lambda kernel, workload: None)
-    assert out["roofline"]["kernel"] == "attn_bwd_short_kernel"
+    out = bench.summarize(w, per, 0.04, 0.06, [0.06], K=1, warmup=0, traffic=lambda kernel, workload: 7)
+    assert set(out["kernels"]) == {"attn_fwd_short_kernel", "attn_bwd_short_kernel", "attn_bwd_reduce_kernel"}
+    r = out["roofline"]
+    assert r["kernel"] == "attn_bwd_short_kernel" and r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["achieved"] == round(b["attn_bwd_short_kernel"] / 0.03e-3 / 1e9, 1) and r["peak"] == 8000
+    assert r["traffic"] == 7
     assert out["bwd_alg_gbps"] == round(bench.alg_bytes(w)[1] / 0.04e-3 / 1e9, 1)
+    assert out["fwd_alg_gbps"] == round(bench.alg_bytes(w)[0] / 0.02e-3 / 1e9, 1)
 
 
 def test_cpu_baseline_record():
