@@ -1,10 +1,12 @@
 """attn_bwd_noalloc (the backward pass on the library's fixed scratch) against attn_bwd.
 
-Two calls in a row on the same GPU, the second with a smaller input, so the
-second runs on a scratch that still holds the first call's contents. Each is
-compared with attn_bwd on a caller workspace (the same kernels: the outputs
-must be bitwise equal), and the smaller one also with the fp64 oracle. Sizes
-whose workspace exceeds the scratch are rejected before anything runs.
+Calls in a row on the same GPU, the second with a smaller input, so later
+calls run on a scratch that still holds an earlier call's contents; the third
+is a batch of 64-token sequences, whose one-kernel backward keeps its dK/dV
+partials at the start of the scratch. Each is compared with attn_bwd on a
+caller workspace (the same kernels: the outputs must be bitwise equal), and
+the smaller ones also with the fp64 oracle. Sizes whose workspace exceeds the
+scratch are rejected before anything runs.
 """
 import math
 
@@ -39,6 +41,7 @@ def test_noalloc_matches_attn_bwd_on_two_calls():
     cases = [  # B, Hq, Hkv, S, D, causal; the first is the Llama-2-70B layer shape (202 MiB of workspace)
         (1, 64, 8, 4096, 128, True),
         (1, 8, 2, 1000, 128, True),
+        (16, 32, 4, 64, 128, True),   # one-kernel backward with 4 head subsets of partials
     ]
     need = [tam.attn_bwd_workspace_bytes(*c[:5]) for c in cases]
     assert need[1] < need[0] <= tam.NOALLOC_SCRATCH_BYTES
@@ -51,7 +54,7 @@ def test_noalloc_matches_attn_bwd_on_two_calls():
             same = torch.equal(g.view(torch.int16), w.view(torch.int16))
             print(f"    {name}: bitwise equal to attn_bwd: {same}", flush=True)
             assert same, name
-        if i == len(cases) - 1:
+        if i >= 1:
             q, k, v, do = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v", "do"))
             ref = att.backward(q, k, v, do, scale, causal=causal)
             for name, g in zip(("dq", "dk", "dv"), got):
