@@ -18,20 +18,21 @@ pytestmark = pytest.mark.gpu
 ONE_BF16 = 0x3F80
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_unit_values_give_unit_output(D):
-    say(f"V = 1, D={D}")
-    x = wl.make_inputs(1, 4, 2, 300, D, seed=(200, D))
+@pytest.mark.parametrize("D,S", [(64, 300), (128, 300), (128, 64)])   # S = 64: the one-kernel forward
+def test_unit_values_give_unit_output(D, S):
+    say(f"V = 1, D={D}, S={S}")
+    x = wl.make_inputs(1, 4, 2, S, D, seed=(200, D))
     x["v"] = np.full_like(x["v"], ONE_BF16)
     gpu = run_gpu(x, True, 1.0 / math.sqrt(D))
     o = to_f64(gpu["o"])
     assert np.max(np.abs(o - 1.0)) <= 4e-3, np.max(np.abs(o - 1.0))
 
 
-@pytest.mark.parametrize("D,mode", [(64, "zero_q"), (128, "zero_q"), (128, "zero_scale")])
-def test_equal_weights_give_running_mean(D, mode):
-    say(f"equal weights ({mode}), D={D}")
-    B, Hq, Hkv, S = 2, 4, 2, 333
+@pytest.mark.parametrize("D,mode,S", [(64, "zero_q", 333), (128, "zero_q", 333), (128, "zero_scale", 333),
+                                      (64, "zero_q", 48), (128, "zero_scale", 64)])   # S <= 64: one-kernel paths
+def test_equal_weights_give_running_mean(D, mode, S):
+    say(f"equal weights ({mode}), D={D}, S={S}")
+    B, Hq, Hkv = 2, 4, 2
     x = wl.make_inputs(B, Hq, Hkv, S, D, seed=(201, D))
     scale = 1.0 / math.sqrt(D)
     if mode == "zero_q":
