@@ -1,7 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
 Tolerances (bf16 outputs vs fp64): max |err| <= 2e-2 and mean |err| <= 2e-3 on
-O, dQ, dK, dV; |err| <= 1e-3 on the fp32 LSE.
+O, dQ, dK, dV, each beyond the rounding a bf16 output cannot avoid (see
+gpu_helpers.assert_close); |err| <= 1e-3 on the fp32 LSE.
 
 Small shapes are compared element by element in full; they span several tiles
 and ragged tails (S not a multiple of the 64/128-row tiles), GQA group sizes
