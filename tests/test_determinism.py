@@ -18,6 +18,8 @@ SHAPES = [
     (1, 16, 2, 1024, 128),   # several dK/dV head subsets: partials + fixed-order sum
     (1, 8, 8, 777, 64),      # one head per group, ragged tail
     (4, 16, 4, 64, 128),     # short sequences
+    (16, 128, 8, 64, 128),   # the batch-16 x 64 workload: one-kernel passes, two head subsets
+    (1, 64, 8, 4096, 128),   # the Llama-2-70B layer at 4096 tokens: fp16 products, two head subsets
 ]
 
 
