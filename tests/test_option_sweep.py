@@ -86,11 +86,13 @@ def test_rope_sweep(case):
     q, k, v, do = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v", "do"))
     rnd = rope.backward(q, k, v, do, scale, causal, base, bf16_rotated=True)
     ext = rope.backward(q, k, v, do, scale, causal, base, bf16_rotated=False)
-    for ref in (rnd, ext):
-        for name in ("o", "dq", "dk", "dv"):
-            assert_close(name, to_f64(g[name]), ref[name])
-        allowance = None if ref is rnd else lse_rounding_allowance(rnd, ext, scale, causal, Hq // Hkv)
-        assert_lse(to_f64(g["lse"]), ref["lse"], allowance)
+    for name in ("o", "dq", "dk", "dv"):
+        assert_close(name, to_f64(g[name]), rnd[name])
+    assert_lse(to_f64(g["lse"]), rnd["lse"])
+    # the unrounded reading, beyond what rounding the rotated inputs moves (tests/test_rope.py)
+    for name in ("o", "dq", "dk", "dv"):
+        assert_close(name, to_f64(g[name]), ext[name], allowance=np.abs(rnd[name] - ext[name]))
+    assert_lse(to_f64(g["lse"]), ext["lse"], lse_rounding_allowance(rnd, ext, scale, causal, Hq // Hkv))
 
 
 @pytest.mark.parametrize("case", _decode_cases(), ids=lambda c: "B{}_Hq{}_Hkv{}_Sq{}_Sk{}_D{}_{}".format(
