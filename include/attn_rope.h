@@ -18,9 +18,8 @@
  * query row, and K once into the workspace (it is shared by the group's query
  * heads); the backward pass rotates Q and K into the workspace and turns dQ
  * and dK back (the inverse rotation) inside the kernels that produce them,
- * before their bf16 rounding. Angles, their (cos, sin) table and the rotation
- * itself are fp64; each rotated value is rounded to bf16 once (nearest, ties to
- * even) and enters the bf16 products so, identically in both passes.
+ * before their bf16 rounding. Angles are formed in fp64. The rotated values
+ * enter the bf16 products rounded to bf16, identically in both passes.
  *
  * Arguments, layout, outputs, errors and limits are those of attn_fwd and
  * attn_bwd in attn.h, plus base (finite and > 0, else ATTN_ERR_BAD_SCALE) and

@@ -18,7 +18,7 @@ from oracle import dropout as dr
 from oracle import rope
 from test_decode import run_decode
 from test_dropout import run as run_dropout
-from test_rope import lse_rounding_allowance
+from test_rope import check_both_readings
 from test_rope import run as run_rope
 from tiled_attention_memory_amd import workloads as wl
 
@@ -86,13 +86,8 @@ def test_rope_sweep(case):
     q, k, v, do = (att.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v", "do"))
     rnd = rope.backward(q, k, v, do, scale, causal, base, bf16_rotated=True)
     ext = rope.backward(q, k, v, do, scale, causal, base, bf16_rotated=False)
-    for name in ("o", "dq", "dk", "dv"):
-        assert_close(name, to_f64(g[name]), rnd[name])
-    assert_lse(to_f64(g["lse"]), rnd["lse"])
-    # the unrounded reading, beyond what rounding the rotated inputs moves (tests/test_rope.py)
-    for name in ("o", "dq", "dk", "dv"):
-        assert_close(name, to_f64(g[name]), ext[name], allowance=np.abs(rnd[name] - ext[name]))
-    assert_lse(to_f64(g["lse"]), ext["lse"], lse_rounding_allowance(rnd, ext, scale, causal, Hq // Hkv))
+    # both readings, with their allowances (tests/test_rope.py)
+    check_both_readings(g, q, k, rnd, ext, scale, causal, base, Hq // Hkv)
 
 
 @pytest.mark.parametrize("case", _decode_cases(), ids=lambda c: "B{}_Hq{}_Hkv{}_Sq{}_Sk{}_D{}_{}".format(

@@ -381,7 +381,7 @@ struct DkdvArgs {
   float c;      // scale * log2(e)
   float scale;
   DropParams drop;  // dropout on the probabilities (DROP kernels only)
-  const double2* rope_inv;  // (cos, sin) table [Sk][D/2]: rotate dK back; null = none
+  const float2* rope_inv;  // (cos, sin) table [Sk][D/2]: rotate dK back; null = none
   // fp16 kernels: q and dout are the dQ kernel's fp16 copies, and these its
   // block exponents of Q, dO and the exact Delta ([B*Hq][ceil(Sq/32)])
   const int* eq;
@@ -867,13 +867,13 @@ void attn_bwd_dkdv_kernel(DkdvArgs a) {
       // dK of the rotated keys back to the unrotated ones: element v of
       // block db is column 32db + 8(v/4) + 4half + v%4, its partner d + D/2
       // sits in block db + DB/2 of this lane
-      const double2* cs = a.rope_inv + (size_t)kvrow * (D / 2);
+      const float2* cs = a.rope_inv + (size_t)kvrow * (D / 2);
 #pragma unroll
       for (int db = 0; db < DB / 2; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           float lo, hi;
-          rope_unrotate(acc[db][v], acc[db + DB / 2][v], cs[32 * db + 8 * (v >> 2) + 4 * half + (v & 3)], &lo, &hi);
+          rope_pair(acc[db][v], acc[db + DB / 2][v], cs[32 * db + 8 * (v >> 2) + 4 * half + (v & 3)], true, &lo, &hi);
           acc[db][v] = lo;
           acc[db + DB / 2][v] = hi;
         }
@@ -962,7 +962,7 @@ struct DqArgs {
   float c;
   float scale;
   DropParams drop;  // dropout on the probabilities (DROP kernels only)
-  const double2* rope_inv;  // (cos, sin) table [Sq][D/2]: rotate dQ back (final mode); null = none
+  const float2* rope_inv;  // (cos, sin) table [Sq][D/2]: rotate dQ back (final mode); null = none
   int pack;  // log2 of the query heads a unit holds (Sq <= kQBR >> pack)
   TileSched sched;
 };
@@ -1471,13 +1471,13 @@ void attn_bwd_dq_kernel(DqArgs a) {
     if (a.rope_inv) {
       // back to the unrotated queries: the partner d + D/2 of column d sits in
       // block db + DB/2 of this lane
-      const double2* cs = a.rope_inv + (size_t)qrow * (D / 2);
+      const float2* cs = a.rope_inv + (size_t)qrow * (D / 2);
 #pragma unroll
       for (int db = 0; db < DB / 2; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           float lo, hi;
-          rope_unrotate(acc[db][v], acc[db + DB / 2][v], cs[32 * db + 8 * (v >> 2) + 4 * half + (v & 3)], &lo, &hi);
+          rope_pair(acc[db][v], acc[db + DB / 2][v], cs[32 * db + 8 * (v >> 2) + 4 * half + (v & 3)], true, &lo, &hi);
           acc[db][v] = lo;
           acc[db + DB / 2][v] = hi;
         }

@@ -419,31 +419,13 @@ __device__ __forceinline__ u32x4 byte_transpose(u32x4 w) {
 
 // Rotary position embedding (rotate-half pairing): the pair (x_d, x_{d+D/2})
 // of a row at position m turns by a_d = m * base^(-2d/D). The table holds
-// (cos a_d, sin a_d) per position and d < D/2 in fp64.
-//
-// The rotated inputs of the products: the rotation runs in fp64 and each value
-// is rounded to bf16 once, nearest with ties to even. (Rotating in fp32 and
-// rounding that would round a value lying within an fp32 rounding of a bf16
-// midpoint to the other neighbour, now and then.) One helper serves every
-// kernel, so a rotated value is bit-identical wherever it is formed.
-__device__ __forceinline__ uint32_t bf16_bits_of(double x) {
-  uint32_t u = __builtin_bit_cast(uint32_t, (float)x);
-  // (float)x landed exactly on a midpoint between two bf16 values: step one
-  // fp32 ulp towards x, so that the rounding below goes x's way
-  if ((u & 0xffffu) == 0x8000u && (double)__builtin_bit_cast(float, u) != x)
-    u = __builtin_fabs(x) > __builtin_fabs((double)__builtin_bit_cast(float, u)) ? u + 1 : u - 1;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-// the pair (lo, hi) of bf16 inputs rotated forward, as bf16 bits
-__device__ __forceinline__ void rope_rotate_bf16(float lo, float hi, double2 cs, uint32_t* out_lo, uint32_t* out_hi) {
-  *out_lo = bf16_bits_of(__builtin_fma((double)lo, cs.x, -((double)hi * cs.y)));
-  *out_hi = bf16_bits_of(__builtin_fma((double)hi, cs.x, (double)lo * cs.y));
-}
-// fp32 gradients turned back (the inverse rotation), before their bf16 rounding
-__device__ __forceinline__ void rope_unrotate(float lo, float hi, double2 cs, float* out_lo, float* out_hi) {
-  const float c = (float)cs.x, sn = -(float)cs.y;
-  *out_lo = __builtin_fmaf(lo, c, -(hi * sn));
-  *out_hi = __builtin_fmaf(hi, c, lo * sn);
+// (cos a_d, sin a_d) per position and d < D/2, computed from fp64 angles. One
+// helper serves every kernel so that a rotated value is bit-identical
+// wherever it is formed; inverse = 1 turns the other way (gradients).
+__device__ __forceinline__ void rope_pair(float lo, float hi, float2 cs, bool inverse, float* out_lo, float* out_hi) {
+  const float sn = inverse ? -cs.y : cs.y;
+  *out_lo = __builtin_fmaf(lo, cs.x, -(hi * sn));
+  *out_hi = __builtin_fmaf(hi, cs.x, lo * sn);
 }
 
 // Scheduler shared by the kernels: work unit = (stream, tile), a stream being

@@ -51,7 +51,7 @@ struct FwdArgs {
   int Hq, Hkv, Sq, Sk, dlt;
   float c;  // softmax scale * log2(e): scores are exponentiated in base 2
   DropParams drop;  // dropout on the probabilities (DROP kernels only)
-  const double2* rope;  // (cos, sin) table [Sq][D/2]: rotate the Q rows at load; null = none
+  const float2* rope;  // (cos, sin) table [Sq][D/2]: rotate the Q rows at load; null = none
   int pack;            // log2 of the query heads a unit holds (Sq <= kBR >> pack)
   TileSched sched;
 };
@@ -113,17 +113,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     if (a.rope && row_ok) {
       // rotary embedding at load: this lane holds elements 16 ks + 8 half + t,
       // and the partner of element d < D/2 (d + D/2) sits in chunk ks + KS/2
-      const double2* cs = a.rope + (size_t)tok * (D / 2);
+      const float2* cs = a.rope + (size_t)tok * (D / 2);
 #pragma unroll
       for (int ks = 0; ks < KS / 2; ++ks)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 16 * ks + 8 * half + 2 * j;
-          uint32_t l0, l1, h0, h1;
-          rope_rotate_bf16(bf16_lo(w[ks][j]), bf16_lo(w[ks + KS / 2][j]), cs[d], &l0, &h0);
-          rope_rotate_bf16(bf16_hi(w[ks][j]), bf16_hi(w[ks + KS / 2][j]), cs[d + 1], &l1, &h1);
-          w[ks][j] = l0 | (l1 << 16);
-          w[ks + KS / 2][j] = h0 | (h1 << 16);
+          float l0, l1, h0, h1;
+          rope_pair(bf16_lo(w[ks][j]), bf16_lo(w[ks + KS / 2][j]), cs[d], false, &l0, &h0);
+          rope_pair(bf16_hi(w[ks][j]), bf16_hi(w[ks + KS / 2][j]), cs[d + 1], false, &l1, &h1);
+          w[ks][j] = pack_bf16(l0, l1);
+          w[ks + KS / 2][j] = pack_bf16(h0, h1);
         }
     }
 #pragma unroll

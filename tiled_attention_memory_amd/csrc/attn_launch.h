@@ -23,7 +23,7 @@ struct AttnShape {
   unsigned long long seed = 0;
   // rotary embedding: (cos, sin) table [S][D/2] in device memory; the forward
   // kernel rotates Q with it at load, the backward kernels rotate dQ and dK back
-  const double2* rope = nullptr;
+  const float2* rope = nullptr;
 };
 
 // Query-stationary kernels give each unit `rows` query rows. A shorter

@@ -7,11 +7,10 @@
 // with d + D/2 and turns by m * base^(-2d/D) at position m.
 //
 //   attn_rope_table_kernel: (cos, sin) per position and pair, from fp64
-//       angles (so that long positions keep their accuracy), stored as fp64.
+//       angles (so that long positions keep their accuracy), stored as fp32.
 //   attn_rope_apply_kernel: a rotated bf16 copy of a [rows, D] tensor
 //       (rows run over batch, head and position), with the same pair helper
-//       the forward kernel uses on its Q rows, so both give identical bits:
-//       the rotation in fp64, each value rounded to bf16 once.
+//       the forward kernel uses on its Q rows, so both give identical bits.
 // HBM-bound elementwise passes; the attention kernels take the table too.
 #include <math.h>
 
@@ -23,19 +22,19 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void attn_rope_table_kernel(double2* tab, int S, int half_d, double base) {
+__global__ __launch_bounds__(kThreads) void attn_rope_table_kernel(float2* tab, int S, int half_d, double base) {
   const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= (long long)S * half_d) return;
   const int m = (int)(idx / half_d), d = (int)(idx % half_d);
   const double ang = (double)m * pow(base, -(double)d / (double)half_d);
   double sn, cs;
   sincos(ang, &sn, &cs);
-  tab[idx] = make_double2(cs, sn);
+  tab[idx] = make_float2((float)cs, (float)sn);
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_rope_apply_kernel(const uint16_t* x, uint16_t* out,
-                                                                   const double2* tab, long long rows, int S) {
+                                                                   const float2* tab, long long rows, int S) {
   constexpr int TPR = D / 16;  // threads per row: 8 pairs each
   const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= rows * TPR) return;
@@ -44,15 +43,15 @@ __global__ __launch_bounds__(kThreads) void attn_rope_apply_kernel(const uint16_
   const int pos = (int)(row % S);
   const u32x4 lo = *reinterpret_cast<const u32x4*>(x + row * D + d0);
   const u32x4 hi = *reinterpret_cast<const u32x4*>(x + row * D + D / 2 + d0);
-  const double2* cs = tab + (size_t)pos * (D / 2) + d0;
+  const float2* cs = tab + (size_t)pos * (D / 2) + d0;
   u32x4 ol, oh;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint32_t l0, l1, h0, h1;
-    rope_rotate_bf16(bf16_lo(lo[j]), bf16_lo(hi[j]), cs[2 * j], &l0, &h0);
-    rope_rotate_bf16(bf16_hi(lo[j]), bf16_hi(hi[j]), cs[2 * j + 1], &l1, &h1);
-    ol[j] = l0 | (l1 << 16);
-    oh[j] = h0 | (h1 << 16);
+    float l0, l1, h0, h1;
+    rope_pair(bf16_lo(lo[j]), bf16_lo(hi[j]), cs[2 * j], false, &l0, &h0);
+    rope_pair(bf16_hi(lo[j]), bf16_hi(hi[j]), cs[2 * j + 1], false, &l1, &h1);
+    ol[j] = pack_bf16(l0, l1);
+    oh[j] = pack_bf16(h0, h1);
   }
   *reinterpret_cast<u32x4*>(out + row * D + d0) = ol;
   *reinterpret_cast<u32x4*>(out + row * D + D / 2 + d0) = oh;
@@ -60,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void attn_rope_apply_kernel(const uint16_
 
 }  // namespace
 
-hipError_t launch_rope_table(double2* tab, int S, int D, double base, hipStream_t stream) {
+hipError_t launch_rope_table(float2* tab, int S, int D, double base, hipStream_t stream) {
   const long long n = (long long)S * (D / 2);
   int half_d = D / 2;
   void* args[] = {(void*)&tab, (void*)&S, (void*)&half_d, (void*)&base};
@@ -68,7 +67,7 @@ hipError_t launch_rope_table(double2* tab, int S, int D, double base, hipStream_
                          dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), args, 0, stream);
 }
 
-hipError_t launch_rope_apply(const uint16_t* x, uint16_t* out, const double2* tab, long long rows, int S, int D,
+hipError_t launch_rope_apply(const uint16_t* x, uint16_t* out, const float2* tab, long long rows, int S, int D,
                              hipStream_t stream) {
   const long long n = rows * (D / 16);
   void* args[] = {(void*)&x, (void*)&out, (void*)&tab, (void*)&rows, (void*)&S};
@@ -83,7 +82,7 @@ RopeLayout rope_layout(const AttnShape& sh) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   RopeLayout L;
   L.table = 0;
-  L.k_rot = al((size_t)sh.Sq * (sh.D / 2) * sizeof(double2));
+  L.k_rot = al((size_t)sh.Sq * (sh.D / 2) * sizeof(float2));
   L.q_rot = L.k_rot + al((size_t)sh.B * sh.Hkv * sh.Sk * sh.D * 2);
   L.bwd = L.q_rot + al((size_t)sh.B * sh.Hq * sh.Sq * sh.D * 2);
   L.total = L.bwd + bwd_workspace_bytes(sh);
@@ -94,7 +93,7 @@ hipError_t launch_fwd_rope(AttnShape sh, const uint16_t* q, const uint16_t* k, c
                            float* lse, void* workspace, double base, hipStream_t stream) {
   const RopeLayout L = rope_layout(sh);
   char* ws = static_cast<char*>(workspace);
-  double2* tab = reinterpret_cast<double2*>(ws + L.table);
+  float2* tab = reinterpret_cast<float2*>(ws + L.table);
   uint16_t* k_rot = reinterpret_cast<uint16_t*>(ws + L.k_rot);
   hipError_t e = launch_rope_table(tab, sh.Sq, sh.D, base, stream);
   if (e == hipSuccess) e = launch_rope_apply(k, k_rot, tab, (long long)sh.B * sh.Hkv * sh.Sk, sh.Sk, sh.D, stream);
@@ -108,7 +107,7 @@ hipError_t launch_bwd_rope(AttnShape sh, const uint16_t* q, const uint16_t* k, c
                            void* workspace, double base, hipStream_t stream) {
   const RopeLayout L = rope_layout(sh);
   char* ws = static_cast<char*>(workspace);
-  double2* tab = reinterpret_cast<double2*>(ws + L.table);
+  float2* tab = reinterpret_cast<float2*>(ws + L.table);
   uint16_t* k_rot = reinterpret_cast<uint16_t*>(ws + L.k_rot);
   uint16_t* q_rot = reinterpret_cast<uint16_t*>(ws + L.q_rot);
   hipError_t e = launch_rope_table(tab, sh.Sq, sh.D, base, stream);
