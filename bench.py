@@ -92,10 +92,12 @@ def device_facts(hip):
             "bf16_peak_at_max_sclk_tflops": round(cus * 4096 * sclk_mhz * 1e6 / 1e12, 1)}
 
 
-def hbm_probe(hip, mib, reps=20):
+def hbm_probe(hip, mib, reps=20, flush=None, flush_mode="read"):
     """Achievable HBM bandwidth with plain library kernels on buffers of `mib` MiB: sequential
     write (fill), read (sum), copy, and a gather of random 4 KiB blocks. GB/s = bytes moved over
-    the median event time of `reps` runs after two warm-up runs."""
+    the median event time of `reps` runs after two warm-up runs. With `flush` (a device buffer)
+    each timed run starts after the buffer is read (or overwritten), outside the events, so that
+    small buffers are timed from HBM rather than from the caches."""
     import torch
     n = (mib << 20) // 4
     a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -117,7 +119,12 @@ def hbm_probe(hip, mib, reps=20):
         for _ in range(2):
             fn()
         times = []
-        for _ in range(reps):
+        for i in range(reps):
+            if flush is not None:
+                if flush_mode == "write":
+                    flush.fill_(float(i))
+                else:
+                    flush.sum()
             e0, e1 = hip.event(), hip.event()
             hip.record(e0, sh)
             fn()
@@ -521,10 +528,14 @@ def main():
     tam.load()  # fail loudly if the HIP library is missing
     if args.hbm_probe:
         hip = Hip()
-        res = hbm_probe(hip, args.hbm_probe)
+        flush = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda")
+                 if args.flush_mib else None)
+        res = hbm_probe(hip, args.hbm_probe, flush=flush, flush_mode=args.flush_mode)
+        cache = "warm" if flush is None else "cold" if args.flush_mode == "read" else "cold, after a write"
         print(json.dumps({"metric": "achievable HBM bandwidth of library kernels", "value": res["copy"]["gbps"],
                           "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "peak_gbps": 8000.0,
-                          "buffer_mib": args.hbm_probe, "probes": res, "device": device_facts(hip)}))
+                          "buffer_mib": args.hbm_probe, "cache": cache, "probes": res,
+                          "device": device_facts(hip)}))
         return
     w = wl.BY_NAME[args.workload]
     log(f"[bench] workload {w.name}: {w.describe()}")
