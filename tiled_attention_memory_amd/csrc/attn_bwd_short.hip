@@ -12,10 +12,13 @@
 // The general path instead needs three kernels (dQ, dK/dV, reduce), reads Q
 // and dO twice and O once.
 //
-// Unit: (batch, kv head, subset of the group's query heads), 4 waves, one per
-// SIMD. K and V stay in LDS for the whole unit; the subset's query heads
-// stream through two LDS stages (Q and dO of the next head load while this
-// one is computed), and dK, dV accumulate over the heads in registers. Per
+// Unit: (batch, kv head, subset of the group's query heads), 8 waves in two
+// groups of four, two waves per SIMD. K and V stay in LDS for the whole unit;
+// the groups take the subset's heads in pairs, one head each, side by side,
+// each group in its own LDS region. The next pair's Q and dO load into
+// registers while a pair is computed and go to LDS once it is done. dK and dV
+// accumulate over each group's heads in registers; at the end group 1 hands
+// its sums to group 0 through LDS, which adds them in that fixed order. Per
 // head, with the 64 queries and 64 keys cut into 32 x 32 quadrants:
 //   1. wave (qh, kb) forms quadrant (queries 32 qh.., keys 32 kb..) of S^T
 //      and dP^T, P and its half of each row's Delta; the two halves of Delta
@@ -38,7 +41,7 @@
 namespace tam {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;       // two groups of four waves
 constexpr int kShortKeys = 64;      // the one key tile
 constexpr long long kShortUnits = 256;  // one unit per compute unit, at least
 
@@ -57,17 +60,18 @@ struct ShortArgs {
   float scale;
 };
 
-// LDS: K, V, two stages of (Q, dO), then the [query][key] tiles of P and dS
-// (hi and lo parts) and the two halves of Delta per row.
+// LDS: K and V, then a region for each group of four waves: its head's Q and
+// dO, and the [query][key] tiles of P and dS (hi and lo parts).
 template <int D>
 struct ShortLayout {
   using T = SwzTile<D>;
   using TP = SwzTile<64>;
   static constexpr int K0 = 0, V0 = T::BYTES;
-  static constexpr int X0 = 2 * T::BYTES;  // stage s: Q at X0 + 2 s T, dO at X0 + (2 s + 1) T
-  static constexpr int PH = 6 * T::BYTES, PL = PH + TP::BYTES, DH = PL + TP::BYTES, DL = DH + TP::BYTES;
-  static constexpr int DEL = DL + TP::BYTES;  // float [2][64]: key block kb's part of Delta, by row
-  static constexpr int BYTES = DEL + 2 * 64 * 4;
+  static constexpr int G0 = 2 * T::BYTES;     // group g's region at G0 + g GBYTES
+  static constexpr int XQ = 0, XD = T::BYTES;  // within a region
+  static constexpr int PH = 2 * T::BYTES, PL = PH + TP::BYTES, DH = PL + TP::BYTES, DL = DH + TP::BYTES;
+  static constexpr int GBYTES = DL + TP::BYTES;
+  static constexpr int BYTES = G0 + 2 * GBYTES;
 };
 
 // hi = bf16(x), lo = bf16(x - hi) for four values, packed in pairs.
@@ -90,9 +94,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_short_kernel(ShortArgs a
   constexpr int KS = D / 16;          // MFMA k-steps over the head dim
   constexpr int DB = D / 32;          // 32-wide head-dim blocks
   constexpr int DBQ = DB / 2;         // of them per wave in step 2
-  constexpr int NLD = T::LOADS / 4;   // 1-KiB loads per wave per tile
-  static_assert(T::ROWS == kShortKeys && TP::ROW_BYTES == 128, "tiles");
+  constexpr int NKV = T::LOADS / 8;   // 1-KiB loads per wave per K or V tile (eight waves)
+  constexpr int NX = T::LOADS / 4;    // per Q or dO tile (the group's four waves)
+  static_assert(T::ROWS == kShortKeys && TP::ROW_BYTES == 128 && NKV >= 1, "tiles");
   static_assert(L::BYTES <= 160 * 1024, "LDS");
+  static_assert(4 * DB * 16 * 64 * 4 <= L::GBYTES, "the dK/dV sums of a group fit its region");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
 
   const int S = a.S;
@@ -104,32 +110,54 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_short_kernel(ShortArgs a
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
+  const int gw = wave >> 2, w4 = wave & 3;  // the wave's group and its place in it
   const int col = lane & 31, half = lane >> 5;
   const int i16 = lane & 15, dsub = 16 * ((lane >> 4) & 1);
-  const int qh = wave >> 1, kb = wave & 1;  // steps 1 and 2: quadrant (qh, kb)
-  const int kb3 = wave >> 1;                // step 3: key block kb3 of dV^T (wave even) or dK^T (odd)
-  const bool dk_role = wave & 1;
+  const int qh = w4 >> 1, kb = w4 & 1;      // steps 1 and 2: quadrant (qh, kb)
+  const int kb3 = w4 >> 1;                  // step 3: key block kb3 of dV^T (w4 even) or dK^T (odd)
+  const bool dk_role = w4 & 1;
   const int q = 32 * qh + col;              // the query row this lane owns in steps 1 and 2
+  const int G = L::G0 + gw * L::GBYTES;     // the group's LDS region
 
-  // Tile loads straight into LDS; rows past S read as zeros. Each wave issues
-  // a quarter of every tile.
-  int loff[NLD];
+  // Tile loads straight into LDS; rows past S read as zeros. K and V: each of
+  // the eight waves issues an eighth; a group's Q and dO: each of its waves a
+  // quarter.
+  int lkv[NKV], lx[NX];
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) loff[i] = T::load_src(wave * NLD + i, lane);
-  auto load_tile = [&](const uint16_t* src, int dst) TAM_INLINE {
+  for (int i = 0; i < NKV; ++i) lkv[i] = T::load_src(wave * NKV + i, lane);
+#pragma unroll
+  for (int i = 0; i < NX; ++i) lx[i] = T::load_src(w4 * NX + i, lane);
+  auto load_kv = [&](const uint16_t* src, int dst) TAM_INLINE {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src, S * D * 2);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) load_lds16(r, smem + dst + (wave * NLD + i) * 1024, loff[i]);
+    for (int i = 0; i < NKV; ++i) load_lds16(r, smem + dst + (wave * NKV + i) * 1024, lkv[i]);
+  };
+  auto load_x = [&](const uint16_t* src, int dst) TAM_INLINE {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, S * D * 2);
+#pragma unroll
+    for (int i = 0; i < NX; ++i) load_lds16(r, smem + dst + (w4 * NX + i) * 1024, lx[i]);
   };
   auto rows_of = [&](const uint16_t* base, int h) TAM_INLINE {
     return base + ((size_t)b * a.Hq + h) * S * D;
   };
   // LSE of this lane's row of head h, and LSE * log2(e) from it (+inf for a
   // row that sees no key or lies past the end: all its probabilities are 0).
-  // The two are apart so that the next head's value loads with its tiles and
-  // is not waited for before them.
+  // The two are apart so that the next head's value loads during this one.
   auto lse_of = [&](int h) TAM_INLINE { return q < S ? a.lse[((size_t)b * a.Hq + h) * S + q] : -INFINITY; };
   auto lse2_from = [&](float l) TAM_INLINE { return l == -INFINITY ? INFINITY : l * kLog2e; };
+  // The next pair's Q and dO come through registers while this pair runs:
+  // lane l holds the 16 bytes that the direct loads would write at LDS byte
+  // 1024 i + 16 l of the tile, and writes them there once the pair is done.
+  u32x4 nq[NX], nd[NX];
+  auto fetch_x = [&](int h) TAM_INLINE {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(rows_of(a.q, h), S * D * 2);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(rows_of(a.dout, h), S * D * 2);
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      nq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, lx[i], 0, 0));
+      nd[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, lx[i], 0, 0));
+    }
+  };
 
   // Per-lane offsets of the transposed reads: rows 4 half + (lane & 15) / 4
   // (+ 8 for the second read) of a 16-row block, elements 32 blk + dsub +
@@ -150,81 +178,110 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_short_kernel(ShortArgs a
 #pragma unroll
   for (int hi = 0; hi < 2; ++hi) poff[hi] = TP::elem_off(4 * half + (i16 >> 2) + 8 * hi, kb3 * 32 + dsub + 4 * (i16 & 3));
 
-  // dV^T (even waves) or dK^T (odd waves), head-dim block db x keys 32 kb3 + (0..31)
+  // dV^T (w4 even) or dK^T (w4 odd), head-dim block db x keys 32 kb3 + (0..31),
+  // summed over the group's heads
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  load_tile(a.k + (size_t)grp * S * D, L::K0);
-  load_tile(a.v + (size_t)grp * S * D, L::V0);
-  load_tile(rows_of(a.q, h_first), L::X0);
-  load_tile(rows_of(a.dout, h_first), L::X0 + T::BYTES);
-  float lse2 = lse2_from(lse_of(h_first));
-  wait_loads();
-  __syncthreads();
-
   // quadrant (qh, kb) holds a visible key
   const bool quad = !CAUSAL || kb <= qh;
-  float* const del = reinterpret_cast<float*>(smem + L::DEL);
+  // the two halves of each row's Delta meet in the group's P-hi tile, before P
+  float* const del = reinterpret_cast<float*>(smem + G + L::PH);
+  const int xq = G + L::XQ, xd = G + L::XD;
 
-  for (int i = 0; i < hps; ++i) {
-    const int xq = L::X0 + 2 * (i & 1) * T::BYTES, xd = xq + T::BYTES;  // this head's Q, dO
-    float lse_next = 0.f;
-    if (i + 1 < hps) {
-      // the next head into the other stage, which the last head has finished with
-      const int nq = L::X0 + 2 * ((i + 1) & 1) * T::BYTES;
-      lse_next = lse_of(h_first + i + 1);
-      load_tile(rows_of(a.q, h_first + i + 1), nq);
-      load_tile(rows_of(a.dout, h_first + i + 1), nq + T::BYTES);
+  // The subset's heads in pairs: group 0 takes heads 0, 2, 4, ..., group 1
+  // heads 1, 3, 5, ... Both groups pass the same barriers; with an odd count
+  // group 1 only keeps step on the last pair.
+  const int npairs = (hps + 1) / 2;
+  float lse_cur = -INFINITY, lse_next = -INFINITY;
+  // pair 0 goes straight into LDS with K and V; pair 1 starts into registers
+  load_kv(a.k + (size_t)grp * S * D, L::K0);
+  load_kv(a.v + (size_t)grp * S * D, L::V0);
+  if (gw < hps) {
+    load_x(rows_of(a.q, h_first + gw), xq);
+    load_x(rows_of(a.dout, h_first + gw), xd);
+    lse_cur = lse_of(h_first + gw);
+  }
+  wait_loads();
+  if (2 + gw < hps) {
+    fetch_x(h_first + 2 + gw);
+    lse_next = lse_of(h_first + 2 + gw);
+  }
+  __syncthreads();
+  for (int ip = 0; ip < npairs; ++ip) {
+    const int h = h_first + 2 * ip + gw;
+    const bool live = 2 * ip + gw < hps;  // uniform over the group
+    if (ip > 0) {
+      // this pair's rows, fetched during the last pair, into the freed region;
+      // then the next pair's fetch
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+          *reinterpret_cast<u32x4*>(smem + xq + (w4 * NX + i) * 1024 + 16 * lane) = nq[i];
+          *reinterpret_cast<u32x4*>(smem + xd + (w4 * NX + i) * 1024 + 16 * lane) = nd[i];
+        }
+      }
+      lse_cur = lse_next;
+      if (2 * ip + 2 + gw < hps) {
+        fetch_x(h + 2);
+        lse_next = lse_of(h + 2);
+      }
+      lds_barrier();
     }
+    const float lse2 = lse2_from(lse_cur);
 
     // 1. S^T and dP^T of the quadrant: element v of lane l is key
     //    32 kb + 8 (v / 4) + 4 half + v % 4 of row q
-    f32x16 s = {}, dp = {};
-    if (quad) {
+    float p[16], dp16[16];
+    if (live) {
+      f32x16 s = {}, dp = {};
+      if (quad) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int kr = T::chunk_off(32 * kb + col, 2 * ks + half), qr = T::chunk_off(q, 2 * ks + half);
-        s = mfma32(*reinterpret_cast<const bf16x8*>(smem + L::K0 + kr), *reinterpret_cast<const bf16x8*>(smem + xq + qr), s);
-        dp = mfma32(*reinterpret_cast<const bf16x8*>(smem + L::V0 + kr), *reinterpret_cast<const bf16x8*>(smem + xd + qr), dp);
+        for (int ks = 0; ks < KS; ++ks) {
+          const int kr = T::chunk_off(32 * kb + col, 2 * ks + half), qr = T::chunk_off(q, 2 * ks + half);
+          s = mfma32(*reinterpret_cast<const bf16x8*>(smem + L::K0 + kr), *reinterpret_cast<const bf16x8*>(smem + xq + qr), s);
+          dp = mfma32(*reinterpret_cast<const bf16x8*>(smem + L::V0 + kr), *reinterpret_cast<const bf16x8*>(smem + xd + qr), dp);
+        }
       }
-    }
-    float p[16];
-    float part = 0.f;
+      float part = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = 32 * kb + 8 * (v >> 2) + 4 * half + (v & 3);
-      const bool ok = quad & (key < S) & (!CAUSAL | (key <= q));  // branch-free
-      const float e = fast_exp2(fmaf(s[v], a.c, -lse2));
-      p[v] = ok ? e : 0.f;
-      part = fmaf(p[v], dp[v], part);
+      for (int v = 0; v < 16; ++v) {
+        const int key = 32 * kb + 8 * (v >> 2) + 4 * half + (v & 3);
+        const bool ok = quad & (key < S) & (!CAUSAL | (key <= q));  // branch-free
+        const float e = fast_exp2(fmaf(s[v], a.c, -lse2));
+        p[v] = ok ? e : 0.f;
+        dp16[v] = dp[v];
+        part = fmaf(p[v], dp[v], part);
+      }
+      part = sum_halves(part);  // sum over the quadrant's 32 keys, in both halves
+      if (half == 0) del[kb * 64 + q] = part;
     }
-    part = sum_halves(part);  // sum over the quadrant's 32 keys, in both halves
-    if (half == 0) del[kb * 64 + q] = part;
     lds_barrier();
-    const float delta = del[q] + del[64 + q];  // the same order in both waves of the row
+    const float delta = live ? del[q] + del[64 + q] : 0.f;  // the same order in both waves of the row
+    lds_barrier();  // every wave has its Delta before P is written over it
     // P and dS (row q, four consecutive keys per group) into the [query][key] tiles
-    if (quad) {
+    if (live && quad) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float ds[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ds[r] = p[4 * g + r] * (dp[4 * g + r] - delta);
+        for (int r = 0; r < 4; ++r) ds[r] = p[4 * g + r] * (dp16[4 * g + r] - delta);
         const int off = TP::elem_off(q, 32 * kb + 8 * g + 4 * half);
-        u32x2 h, l;
-        split4(p + 4 * g, &h, &l);
-        *reinterpret_cast<u32x2*>(smem + L::PH + off) = h;
-        *reinterpret_cast<u32x2*>(smem + L::PL + off) = l;
-        split4(ds, &h, &l);
-        *reinterpret_cast<u32x2*>(smem + L::DH + off) = h;
-        *reinterpret_cast<u32x2*>(smem + L::DL + off) = l;
+        u32x2 hv, lv;
+        split4(p + 4 * g, &hv, &lv);
+        *reinterpret_cast<u32x2*>(smem + G + L::PH + off) = hv;
+        *reinterpret_cast<u32x2*>(smem + G + L::PL + off) = lv;
+        split4(ds, &hv, &lv);
+        *reinterpret_cast<u32x2*>(smem + G + L::DH + off) = hv;
+        *reinterpret_cast<u32x2*>(smem + G + L::DL + off) = lv;
       }
     }
     lds_barrier();
 
-    // 2. dQ^T (head-dim blocks DBQ kb .., rows of query half qh) = K^T dS^T:
-    //    A = K^T read transposed, B = dS^T rows of the tiles, k-slots matching
-    {
+    if (live) {
+      // 2. dQ^T (head-dim blocks DBQ kb .., rows of query half qh) = K^T dS^T:
+      //    A = K^T read transposed, B = dS^T rows of the tiles, k-slots matching
       f32x16 dq[DBQ];
 #pragma unroll
       for (int j = 0; j < DBQ; ++j) dq[j] = f32x16{};
@@ -234,10 +291,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_short_kernel(ShortArgs a
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           const int e0 = 32 * kk + 16 * k2 + 4 * half;
-          const u32x2 h0 = *reinterpret_cast<const u32x2*>(smem + L::DH + TP::elem_off(q, e0));
-          const u32x2 h1 = *reinterpret_cast<const u32x2*>(smem + L::DH + TP::elem_off(q, e0 + 8));
-          const u32x2 l0 = *reinterpret_cast<const u32x2*>(smem + L::DL + TP::elem_off(q, e0));
-          const u32x2 l1 = *reinterpret_cast<const u32x2*>(smem + L::DL + TP::elem_off(q, e0 + 8));
+          const u32x2 h0 = *reinterpret_cast<const u32x2*>(smem + G + L::DH + TP::elem_off(q, e0));
+          const u32x2 h1 = *reinterpret_cast<const u32x2*>(smem + G + L::DH + TP::elem_off(q, e0 + 8));
+          const u32x2 l0 = *reinterpret_cast<const u32x2*>(smem + G + L::DL + TP::elem_off(q, e0));
+          const u32x2 l1 = *reinterpret_cast<const u32x2*>(smem + G + L::DL + TP::elem_off(q, e0 + 8));
           const bf16x8 bh = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
           const bf16x8 bl = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
           const unsigned char* kt = smem + L::K0 + (32 * kk + 16 * k2) * T::ROW_BYTES;
@@ -253,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_short_kernel(ShortArgs a
       if (q < S) {
         // lane holds columns 32 db + 8 i + 4 half + (0..3) of row q; pairs of i
         // are merged across the halves into 16-byte stores
-        uint16_t* op = a.dq + ((size_t)b * a.Hq + h_first + i) * S * D + (size_t)q * D + 8 * half;
+        uint16_t* op = a.dq + ((size_t)b * a.Hq + h) * S * D + (size_t)q * D + 8 * half;
 #pragma unroll
         for (int j = 0; j < DBQ; ++j)
 #pragma unroll
@@ -268,12 +325,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_short_kernel(ShortArgs a
             *reinterpret_cast<u32x4*>(op + 32 * (DBQ * kb + j) + 16 * m) = pair_halves(w[0], w[1]);
           }
       }
-    }
 
-    // 3. key block kb3 of dV^T += dO^T P or dK^T += Q^T dS, over 16-row blocks of queries
-    {
+      // 3. key block kb3 of dV^T += dO^T P or dK^T += Q^T dS, over 16-row blocks of queries
       const int xt = dk_role ? xq : xd;
-      const int yh = dk_role ? L::DH : L::PH, yl = dk_role ? L::DL : L::PL;
+      const int yh = G + (dk_role ? L::DH : L::PH), yl = G + (dk_role ? L::DL : L::PL);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         if (CAUSAL && kb3 > qb) continue;  // the empty quadrant
@@ -297,10 +352,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_short_kernel(ShortArgs a
         }
       }
     }
-    wait_loads();   // the next head's tiles
-    __syncthreads();
-    lse2 = lse2_from(lse_next);
+    __syncthreads();  // the group's Q, dO and tiles are free for the next pair
   }
+
+  // Group 1 hands its sums to group 0 through its own region; group 0 adds
+  // them to its own (a fixed order) and stores.
+  float* hand = reinterpret_cast<float*>(smem + L::G0 + L::GBYTES) + w4 * (DB * 16 * 64) + lane;
+  if (gw == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) hand[(16 * db + v) * 64] = acc[db][v];
+  }
+  __syncthreads();
+  if (gw == 1) return;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[db][v] += hand[(16 * db + v) * 64];
 
   // dV^T or dK^T: element v of lane l is head-dim column 32 db + 8 (v / 4) +
   // 4 half + v % 4 of key 32 kb3 + col
