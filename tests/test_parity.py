@@ -70,6 +70,28 @@ def test_small_shapes(shape):
     compare_full(gpu, oracle_full(x, scale, causal))
 
 
+SHORT_SUBSETS = [  # B, Hq, Hkv, S, D, causal: heads per subset of the one-kernel backward
+    (64, 12, 2, 64, 128, True),   # 128 groups, 2 subsets of 3 heads: odd, with partials
+    (32, 40, 8, 48, 64, False),   # 256 groups, 1 subset of 5 heads: odd, dK/dV stored directly
+    (128, 4, 2, 64, 128, True),   # 256 groups, 1 subset of 2 heads: one pair, stored directly
+]
+
+
+@pytest.mark.parametrize("shape", SHORT_SUBSETS, ids=lambda s: "B{}_Hq{}_Hkv{}_S{}_D{}_{}".format(
+    *s[:5], "causal" if s[5] else "full"))
+def test_short_path_head_subsets(shape):
+    """The one-kernel backward at 64 tokens or fewer takes a subset's heads in
+    pairs, one per group of four waves; with an odd count the second group sits
+    out the last pair. With 256 or more (batch, kv head) groups there is one
+    subset and dK, dV are stored directly instead of as partials."""
+    B, Hq, Hkv, S, D, causal = shape
+    say(f"short-path head subsets {shape}")
+    x = wl.make_inputs(B, Hq, Hkv, S, D, seed=(130, B, Hq, Hkv, S, D, int(causal)))
+    scale = 1.0 / math.sqrt(D)
+    gpu = run_gpu(x, causal, scale)
+    compare_full(gpu, oracle_full(x, scale, causal))
+
+
 @pytest.mark.parametrize("w", [wl.WORKLOADS[0], wl.WORKLOADS[2]], ids=lambda w: w.name)
 def test_workload_full(w):
     """The S=256/D=64 and the batch-16 S=64 workloads, every element."""
