@@ -415,9 +415,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 // so the softmax needs no running max and K, V can serve many query heads.
 // Unit: (batch, kv head, subset of the group's query heads), 4 waves. K and V
 // go to LDS once; waves 2p and 2p + 1 take rows 0..31 and 32..63 of the
-// subset's heads p, p + 2, ..., each holding its rows of Q in registers while
-// the next head's rows load. With no barrier after the first, the waves run
-// independently.
+// subset's heads p, p + 2, ..., with their rows of Q in two register sets
+// used in turn: the first two heads' rows load together with K and V, and
+// each later head's rows load while the head two before it is computed. With
+// no barrier after the first, the waves run independently.
 struct FwdShortArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -462,16 +463,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_short_kernel(FwdShortArg
       load_lds16(rv, kv + T::BYTES + li * 1024, T::load_src(li, lane));
     }
   }
+  // This lane's Q chunks of head h through a bounded buffer: rows past S read
+  // as zeros, and every wave issues exactly KS loads.
   auto load_q = [&](int h, u32x4 (&w)[KS]) TAM_INLINE {
-    const uint16_t* qp = a.q + (((size_t)b * a.Hq + h) * S + tok) * D + 8 * half;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + ((size_t)b * a.Hq + h) * S * D, S * D * 2);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) w[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < KS; ++ks)
+      w[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (tok * D + 8 * half + 16 * ks) * 2, 0, 0));
   };
+  // A wave's heads alternate between two register sets, so that the second
+  // head's rows load together with K, V and the first head's rows.
   int h = h_end - hps + (wave >> 1);
-  u32x4 qn[KS];
-  if (h < h_end) load_q(h, qn);
-  wait_loads();
-  __syncthreads();
+  u32x4 qa[KS], qb[KS];
+  if (h < h_end) load_q(h, qa);
+  if (h + 2 < h_end) {
+    __asm__ volatile("" ::: "memory");  // issued after the loads above
+    load_q(h + 2, qb);
+    wait_vm<KS>();   // K, V and the first head's rows; the second head's may still be in flight
+  } else {
+    wait_loads();
+  }
+  // A bare barrier: the wait above has put K and V into LDS, and a full
+  // __syncthreads would also wait for the second head's rows. The empty asm
+  // statements keep the compiler from moving memory accesses across it.
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 
   int koff[KS], voff[DB][2];
   const int i16 = lane & 15;
@@ -552,15 +569,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_short_kernel(FwdShortArg
 
   // rows 0..31 see only keys 0..31 under a causal mask, and so does every row of S <= 32
   const bool one_block = (CAUSAL && rb == 0) || S <= 32;
-  for (; h < h_end; h += 2) {
+  // head hh from the register set w, whose rows are then reloaded for head hh + 4
+  auto step = [&](u32x4 (&w)[KS], int hh) TAM_INLINE {
     bf16x8 qf[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qn[ks] ^ flip);
-    if (h + 2 < h_end) load_q(h + 2, qn);  // the next head's rows load meanwhile
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, w[ks] ^ flip);
+    if (hh + 4 < h_end) load_q(hh + 4, w);
     if (one_block)
-      head(std::integral_constant<int, 1>{}, qf, h);
+      head(std::integral_constant<int, 1>{}, qf, hh);
     else
-      head(std::integral_constant<int, 2>{}, qf, h);
+      head(std::integral_constant<int, 2>{}, qf, hh);
+  };
+  for (; h < h_end; h += 4) {
+    step(qa, h);
+    if (h + 2 < h_end) step(qb, h + 2);
   }
 }
 
