@@ -70,10 +70,15 @@ def test_small_shapes(shape):
     compare_full(gpu, oracle_full(x, scale, causal))
 
 
-SHORT_SUBSETS = [  # B, Hq, Hkv, S, D, causal: heads per subset of the one-kernel backward
+SHORT_SUBSETS = [  # B, Hq, Hkv, S, D, causal: heads per subset of the one-kernel paths
     (64, 12, 2, 64, 128, True),   # 128 groups, 2 subsets of 3 heads: odd, with partials
     (32, 40, 8, 48, 64, False),   # 256 groups, 1 subset of 5 heads: odd, dK/dV stored directly
     (128, 4, 2, 64, 128, True),   # 256 groups, 1 subset of 2 heads: one pair, stored directly
+    # 512 groups: one subset of every head in both kernels; the forward's waves
+    # take three heads (six) or three and two (five), so their two Q register
+    # sets are reloaded, and the backward runs three pairs
+    (64, 48, 8, 64, 128, True),
+    (64, 40, 8, 37, 64, False),
 ]
 
 
@@ -83,7 +88,9 @@ def test_short_path_head_subsets(shape):
     """The one-kernel backward at 64 tokens or fewer takes a subset's heads in
     pairs, one per group of four waves; with an odd count the second group sits
     out the last pair. With 256 or more (batch, kv head) groups there is one
-    subset and dK, dV are stored directly instead of as partials."""
+    subset and dK, dV are stored directly instead of as partials. The
+    one-kernel forward gives each wave every other head of its subset, in two
+    Q register sets used in turn."""
     B, Hq, Hkv, S, D, causal = shape
     say(f"short-path head subsets {shape}")
     x = wl.make_inputs(B, Hq, Hkv, S, D, seed=(130, B, Hq, Hkv, S, D, int(causal)))
